@@ -1,0 +1,48 @@
+"""fp64 CPU oracle for the sequence-parallel DiT attention hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product package imports, links or
+calls this package; only the test suite, the graft smoke check and the
+``cpu_baseline`` leg of ``bench.py`` may use it.  It shares no code, header,
+table or helper with the HIP library: it is written from the source pages'
+definitions, in float64, with numpy as the only numerical library.
+
+Sources (cited by page title and section):
+
+* edge-dit.cpp, "Parallel execution" page -- CFG combine formula (CFG
+  parallelism section); the attention formula after the sequence-to-head
+  redistribution and the Ulysses layouts (Ulysses sequence parallelism
+  section); the SPSequenceSplit / SPAllToAll4DLayout state and the packed
+  peer-major buffers (SP layout and fused operator sections).
+* SGLang Diffusion, "Parallelism Overview" -- the USP shapes ("What happens
+  to the shapes"), the ring merge needing the kernel's LSE ("Constraints"),
+  the all-to-all being a pure permutation ("The Ulysses transport").
+* xLLM, "DiT Architecture and Capability Matrix" -- sequence padding to a
+  multiple of lcm(SP, 64) and padding exclusion ("MiniMax-H3 boundaries").
+* cache-dit, "Context Parallelism" -- head padding before / after the
+  all-to-all ("Any Head Num" under UAA).
+
+Modules:
+  oracle.reference  -- vectorised numpy fp64 definitions (the oracle proper)
+  oracle.brute      -- pure-Python loop versions for tiny inputs (a second,
+                       independently written check of the oracle itself)
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests
+(closed forms, invariants, brute force, library cross-checks); none is
+"parity unpinned".
+"""
+
+from .reference import (  # noqa: F401
+    attention,
+    merge,
+    ring_attention,
+    ring_hop_order,
+    a2a_layout,
+    pack_seq_to_head,
+    unpack_seq_to_head,
+    pack_head_to_seq,
+    unpack_head_to_seq,
+    all_to_all,
+    cfg_combine,
+    cfg_combine_f32,
+    fmaf,
+)

@@ -1,0 +1,337 @@
+"""Plain float64 definitions of every step on the hot path.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): not imported by the
+product package, and it imports nothing from it.
+
+Each function is the definition written out with numpy; a matrix product is
+the only library primitive used as a step.  Where the pages leave a step
+open, the reading taken is stated in the function's docstring.
+
+Tensor conventions (all row-major numpy arrays):
+  Q          [B, Sq,  H, D]
+  K, V       [B, Skv, H, D]
+  O          [B, Sq,  H, D]
+  LSE        [B, H, Sq]      natural log of sum_j exp(scale * q . k_j)
+  send/recv  [U, n_planes, B, S_loc, H_loc, D]   peer-major exchange buffer
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F64 = np.float64
+NEG_INF = -np.inf
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
+# Attention with per-row log-sum-exp
+# ---------------------------------------------------------------------------
+
+def attention(q, k, v, scale: float, rows=None, row_group: int = 1024):
+    """Exact non-causal attention and its per-row LSE.
+
+    Follows edge-dit.cpp "Parallel execution", Ulysses section: after the
+    sequence-to-head redistribution each rank evaluates the full softmax
+    attention O = softmax(Q K^T / sqrt(D)) V for its heads, with no mask and
+    no approximation.  The LSE output is what SGLang's "Parallelism
+    Overview", "Constraints" section requires of a ring-capable kernel.
+
+    For every (b, h, i):
+        s_j   = scale * sum_d q[b,i,h,d] * k[b,j,h,d]
+        m     = max_j s_j
+        l     = sum_j exp(s_j - m)
+        O     = (sum_j exp(s_j - m) * v[b,j,h,:]) / l
+        LSE   = m + ln(l)
+    Skv == 0: O = 0 and LSE = -inf (the identity of ``merge``).
+
+    ``scale`` is the caller's value (a float32 in the library) promoted to
+    float64.  ``rows`` optionally restricts the query rows evaluated (row
+    outputs are independent, so a sample is exact for its rows); the returned
+    arrays then hold only those rows, in the order given.  ``row_group`` only
+    bounds memory: rows are evaluated group by group, each row's arithmetic
+    unchanged.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    if rows is not None:
+        q = q[:, np.asarray(rows, dtype=np.int64)]
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    assert k.shape == (B, Skv, H, D) and v.shape == (B, Skv, H, D)
+    scale = float(scale)
+    o = np.zeros((B, Sq, H, D), dtype=F64)
+    lse = np.full((B, H, Sq), NEG_INF, dtype=F64)
+    if Skv == 0 or Sq == 0:
+        return o, lse
+    for b in range(B):
+        for h in range(H):
+            kh = k[b, :, h, :]
+            vh = v[b, :, h, :]
+            for r0 in range(0, Sq, row_group):
+                r1 = min(Sq, r0 + row_group)
+                s = scale * (q[b, r0:r1, h, :] @ kh.T)          # [rows, Skv]
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)
+                o[b, r0:r1, h, :] = (e @ vh) / l
+                lse[b, h, r0:r1] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Online-softmax merge of partial results (ring hops)
+# ---------------------------------------------------------------------------
+
+def merge(o_a, lse_a, o_c, lse_c):
+    """Combine two partial attention results over disjoint key sets.
+
+    SGLang "Parallelism Overview": the ring per-hop merge and the merge of
+    replicated / tail-padded parts use the online-softmax rule with the
+    kernel's LSE ("What happens to the shapes", "Constraints").
+
+    With m = max(L_a, L_c) and w_x = exp(L_x - m):
+        L = m + ln(w_a + w_c)
+        O = (w_a O_a + w_c O_c) / (w_a + w_c)
+    A part whose LSE is -inf holds no keys: its term is dropped (selected
+    away, never multiplied), so whatever its O holds cannot leak.  If both
+    are -inf the result is (0, -inf).
+    """
+    o_a = _f64(o_a)
+    o_c = _f64(o_c)
+    la = np.transpose(_f64(lse_a), (0, 2, 1))[..., None]   # [B,Sq,H,1]
+    lc = np.transpose(_f64(lse_c), (0, 2, 1))[..., None]
+    m = np.maximum(la, lc)
+    empty = m == NEG_INF
+    m_safe = np.where(empty, 0.0, m)
+    with np.errstate(invalid="ignore", over="ignore"):
+        wa = np.where(la == NEG_INF, 0.0, np.exp(la - m_safe))
+        wc = np.where(lc == NEG_INF, 0.0, np.exp(lc - m_safe))
+    wsum = wa + wc
+    # select before multiplying: a dropped part contributes exactly 0
+    num = wa * np.where(wa > 0, o_a, 0.0) + wc * np.where(wc > 0, o_c, 0.0)
+    o = np.where(empty, 0.0, num / np.where(empty, 1.0, wsum))
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, NEG_INF, m_safe + np.log(np.where(empty, 1.0, wsum)))
+    return o, np.transpose(lse[..., 0], (0, 2, 1)).copy()
+
+
+def ring_hop_order(R: int, rank: int = 0):
+    """Order in which ring rank ``rank`` sees the R key/value chunks.
+
+    Reading (the pages say K/V rotate between neighbours but not which way):
+    a rank first attends its own chunk, then the chunk of its previous
+    neighbour, and so on -- chunk (rank - k) mod R at hop k.
+    """
+    return [(rank - t) % R for t in range(R)]
+
+
+def ring_attention(q, k, v, scale: float, bounds, order=None):
+    """Ring attention of one rank, with its hops run one after another.
+
+    ``bounds`` = [b_0 = 0, b_1, ..., b_R = Skv]: chunk c holds keys
+    [b_c, b_{c+1}) (chunks may be empty or uneven).  The result is the left
+    fold of ``merge`` over the chunk results in ``order`` (default 0..R-1),
+    as SGLang "Parallelism Overview" describes ring attention: Q stays put,
+    each K/V hop yields a partial (O, LSE) that is merged into the running
+    result.
+    """
+    R = len(bounds) - 1
+    if order is None:
+        order = list(range(R))
+    k = _f64(k)
+    v = _f64(v)
+    acc = None
+    for c in order:
+        part = attention(q, k[:, bounds[c]:bounds[c + 1]], v[:, bounds[c]:bounds[c + 1]], scale)
+        acc = part if acc is None else merge(acc[0], acc[1], part[0], part[1])
+    return acc
+
+
+# ---------------------------------------------------------------------------
+# Ulysses all-to-all layout and the pack / unpack permutations
+# ---------------------------------------------------------------------------
+
+def a2a_layout(B, S, H, D, U, seq_align=1, n_planes=1):
+    """Derived sizes of one Ulysses redistribution.
+
+    edge-dit.cpp "Parallel execution": the sequence split records original,
+    padded and local lengths; the all-to-all layout records global and local
+    heads and sequence lengths, batch, head dim and elements per peer.
+
+    Readings:
+      * sequence padding (edge-dit: divisible or padded; xLLM "MiniMax-H3
+        boundaries": padded to a multiple of lcm(SP, 64)):
+        S_pad = ceil(S / lcm(U, seq_align)) * lcm(U, seq_align), S_loc = S_pad / U;
+      * head padding (cache-dit "Any Head Num"): H_pad = ceil(H / U) * U,
+        H_loc = H_pad / U; pad heads are the global indices >= H.
+    """
+    align = U * seq_align // math.gcd(U, seq_align)
+    S_pad = -(-S // align) * align
+    S_loc = S_pad // U
+    H_pad = -(-H // U) * U
+    H_loc = H_pad // U
+    return dict(B=B, S=S, H=H, D=D, U=U, seq_align=seq_align, n_planes=n_planes,
+                S_pad=S_pad, S_loc=S_loc, H_pad=H_pad, H_loc=H_loc,
+                elems_per_peer=n_planes * B * S_loc * H_loc * D)
+
+
+def _gather(src: np.ndarray, idx: np.ndarray, valid: np.ndarray) -> np.ndarray:
+    flat = src.reshape(-1)
+    out = np.zeros(idx.shape, dtype=src.dtype)
+    out[valid] = flat[idx[valid]]
+    return out
+
+
+def pack_seq_to_head(in_planes, L, rank):
+    """Sequence-to-head send buffer of Ulysses rank ``rank``.
+
+    edge-dit.cpp packed QKV operator: the planes are concatenated, split by
+    destination head group and flattened peer-major.  Reading of the order:
+    send[p, pl, b, s, h', d] = in_pl[b, s, p*H_loc + h', d] when the global
+    row rank*S_loc + s < S and the global head p*H_loc + h' < H, else 0.
+    in_planes: n_planes arrays [B, S_loc, H, D] (rows past S never read).
+    Written as a gather: the source flat index of every output element.
+    """
+    U, B, S, H, D = L["U"], L["B"], L["S"], L["H"], L["D"]
+    S_loc, H_loc, n = L["S_loc"], L["H_loc"], L["n_planes"]
+    assert len(in_planes) == n
+    p, pl, b, s, hh, d = np.ix_(np.arange(U), np.arange(n), np.arange(B),
+                                np.arange(S_loc), np.arange(H_loc), np.arange(D))
+    head = p * H_loc + hh
+    valid = (rank * S_loc + s < S) & (head < H)
+    src_idx = (((pl * B + b) * S_loc + s) * H + head) * D + d
+    shape = (U, n, B, S_loc, H_loc, D)
+    valid = np.broadcast_to(valid, shape)
+    src_idx = np.broadcast_to(src_idx, shape)
+    stacked = np.stack([np.asarray(x).reshape(B, S_loc, H, D) for x in in_planes])
+    return _gather(stacked, np.where(valid, src_idx, 0), valid)
+
+
+def unpack_seq_to_head(recv, L, rank):
+    """Head-sharded full-sequence planes from a sequence-to-head receive buffer.
+
+    edge-dit.cpp receive preparation (without RoPE): the rank-major receive
+    buffer is decoded into one [B, S, H_loc, D] tensor per plane:
+    out_pl[b, t, h', d] = recv[t // S_loc, pl, b, t mod S_loc, h', d] for the
+    S real rows t < S.  Pad rows are dropped here, so attention sees exactly
+    the real keys (xLLM: padding exclusion).  ``rank`` does not enter the map.
+    """
+    U, B, S, D = L["U"], L["B"], L["S"], L["D"]
+    S_loc, H_loc, n = L["S_loc"], L["H_loc"], L["n_planes"]
+    pl, b, t, hh, d = np.ix_(np.arange(n), np.arange(B), np.arange(S),
+                             np.arange(H_loc), np.arange(D))
+    src_idx = (((((t // S_loc) * n + pl) * B + b) * S_loc + t % S_loc) * H_loc + hh) * D + d
+    shape = (n, B, S, H_loc, D)
+    src_idx = np.broadcast_to(src_idx, shape)
+    out = _gather(np.asarray(recv), src_idx, np.ones(shape, dtype=bool))
+    return [out[i] for i in range(n)]
+
+
+def pack_head_to_seq(in_planes, L, rank):
+    """Head-to-sequence send buffer of Ulysses rank ``rank``.
+
+    edge-dit.cpp packed head-to-sequence operator: the head-sharded output
+    is split by destination sequence shard and flattened peer-major:
+    send[p, pl, b, s, h', d] = in_pl[b, p*S_loc + s, h', d] when
+    p*S_loc + s < S and rank*H_loc + h' < H, else 0.
+    in_planes: n_planes arrays [B, S, H_loc, D].
+    """
+    U, B, S, H, D = L["U"], L["B"], L["S"], L["H"], L["D"]
+    S_loc, H_loc, n = L["S_loc"], L["H_loc"], L["n_planes"]
+    assert len(in_planes) == n
+    p, pl, b, s, hh, d = np.ix_(np.arange(U), np.arange(n), np.arange(B),
+                                np.arange(S_loc), np.arange(H_loc), np.arange(D))
+    row = p * S_loc + s
+    valid = (row < S) & (rank * H_loc + hh < H)
+    src_idx = (((pl * B + b) * S + row) * H_loc + hh) * D + d
+    shape = (U, n, B, S_loc, H_loc, D)
+    valid = np.broadcast_to(valid, shape)
+    src_idx = np.broadcast_to(src_idx, shape)
+    stacked = np.stack([np.asarray(x).reshape(B, S, H_loc, D) for x in in_planes])
+    return _gather(stacked, np.where(valid, src_idx, 0), valid)
+
+
+def unpack_head_to_seq(recv, L, rank):
+    """Sequence-sharded planes from a head-to-sequence receive buffer.
+
+    edge-dit.cpp receive-side unpack of the head-to-sequence path:
+    out_pl[b, s, h, d] = recv[h // H_loc, pl, b, s, h mod H_loc, d] for the
+    H real heads (pad heads dropped); local rows whose global index
+    rank*S_loc + s >= S are pad rows and are written as 0.
+    Output: n_planes arrays [B, S_loc, H, D].
+    """
+    U, B, S, H, D = L["U"], L["B"], L["S"], L["H"], L["D"]
+    S_loc, H_loc, n = L["S_loc"], L["H_loc"], L["n_planes"]
+    pl, b, s, h, d = np.ix_(np.arange(n), np.arange(B), np.arange(S_loc),
+                            np.arange(H), np.arange(D))
+    src_idx = (((((h // H_loc) * n + pl) * B + b) * S_loc + s) * H_loc + h % H_loc) * D + d
+    valid = rank * S_loc + s < S
+    shape = (n, B, S_loc, H, D)
+    valid = np.broadcast_to(valid, shape)
+    src_idx = np.broadcast_to(src_idx, shape)
+    out = _gather(np.asarray(recv), np.where(valid, src_idx, 0), valid)
+    return [out[i] for i in range(n)]
+
+
+def all_to_all(sends):
+    """The exchange itself (a test helper; the library never performs it).
+
+    recv_r[p] = send_p[r]: the chunk rank p addressed to rank r.  SGLang
+    "The Ulysses transport": an all-to-all only permutes data.
+    """
+    U = len(sends)
+    return [np.stack([sends[p][r] for p in range(U)]) for r in range(U)]
+
+
+# ---------------------------------------------------------------------------
+# Classifier-free guidance combine
+# ---------------------------------------------------------------------------
+
+def cfg_combine(u, c, g: float):
+    """edge-dit.cpp "Parallel execution", CFG section: the guided prediction
+    is p_uncond + g * (p_cond - p_uncond); evaluated here in float64."""
+    u = _f64(u)
+    c = _f64(c)
+    return u + float(g) * (c - u)
+
+
+def fmaf(a, b, c):
+    """Correctly rounded float32 fused multiply-add of float32 arrays.
+
+    a*b is exact in float64 (24 + 24 significant bits).  The float64 sum is
+    formed with rounding to odd -- round to nearest, then, when the TwoSum
+    error (Knuth) is non-zero and the last significand bit is even, step one
+    ulp toward the error -- and the result rounded once more to float32.
+    Boldo and Melquiond (IEEE Trans. Computers, 2008) prove that this double
+    rounding equals a single rounding of the exact a*b + c when the
+    intermediate format has at least 2p + 2 bits (53 >= 2*24 + 2).
+    """
+    a = np.asarray(a, dtype=np.float32).astype(F64)
+    b = np.asarray(b, dtype=np.float32).astype(F64)
+    c = np.asarray(c, dtype=np.float32).astype(F64)
+    p = a * b
+    s = p + c
+    bb = s - p
+    err = (p - (s - bb)) + (c - bb)
+    even = (s.view(np.int64) & 1) == 0
+    fix = (err != 0) & even & np.isfinite(s)
+    toward = np.where(err > 0, np.inf, -np.inf)
+    s = np.where(fix, np.nextafter(s, toward), s)
+    return s.astype(np.float32)
+
+
+def cfg_combine_f32(u, c, g: float):
+    """The float32 evaluation the library performs: d = fl32(c - u), then one
+    fused multiply-add g*d + u, rounded once (the same formula as
+    ``cfg_combine``, at float32)."""
+    u = np.asarray(u, dtype=np.float32)
+    c = np.asarray(c, dtype=np.float32)
+    d = (c - u).astype(np.float32)
+    return fmaf(np.float32(g), d, u)
