@@ -1,0 +1,222 @@
+/*
+ * dit_attn.h -- C ABI of the per-GPU hot path of sequence-parallel DiT
+ * attention on AMD Instinct MI355X (gfx950).
+ *
+ * One rank's share of a Ulysses x ring split is computed by five kinds of
+ * call:
+ *   dit_ulysses_pack / dit_ulysses_unpack  layout transforms around the
+ *                                          Ulysses all-to-alls
+ *   dit_attn_fwd                           attention with per-row LSE
+ *   dit_attn_merge                         online-softmax merge of partial
+ *                                          results (ring hops)
+ *   dit_cfg_combine                        classifier-free guidance combine
+ *
+ * Shapes follow SGLang Diffusion "Parallelism Overview" ("What happens to
+ * the shapes"): sequence-sharded [B, S/(U*R), H/T, D] outside attention,
+ * head-sharded [B, S/R, H/(T*U), D] inside it.  In this header S denotes the
+ * sequence of one Ulysses group (S/R globally) and H the heads entering the
+ * Ulysses split (H/T globally).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major tensors,
+ *     owned by the caller.  The library never allocates, frees or retains
+ *     device memory and keeps no state between calls (thread-safe and
+ *     reentrant; only the per-thread error text is stored).
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*,
+ *     NULL = the default stream) and never synchronizes.
+ *   - All validation happens before any launch; on an error nothing is
+ *     written and the call returns a non-zero status whose detail
+ *     dit_last_error() gives.  DIT_ERR_UNSUPPORTED means "valid request that
+ *     this library does not serve": the caller should fall back to generic
+ *     operators (edge-dit.cpp "Parallel execution": unsupported shapes or
+ *     dtypes take the generic operator path).
+ *   - Tensor pointers of attention, merge and CFG calls must be 16-byte
+ *     aligned (LSE: 4-byte); permute pointers need only element alignment
+ *     (DIT_ERR_UNSUPPORTED otherwise).
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_ABI_VERSION 1
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad enum, rank out of range */
+  DIT_ERR_UNSUPPORTED = 2,      /* valid but not served: head dim, dtype, alignment */
+  DIT_ERR_HIP = 3               /* a kernel launch failed */
+} dit_status_t;
+
+typedef enum { DIT_BF16 = 0, DIT_F16 = 1, DIT_F32 = 2 } dit_dtype_t;
+
+typedef enum {
+  DIT_SEQ_TO_HEAD = 0, /* sequence-sharded -> head-sharded (before attention) */
+  DIT_HEAD_TO_SEQ = 1  /* head-sharded -> sequence-sharded (after attention) */
+} dit_a2a_dir_t;
+
+/*
+ * Layout of one Ulysses redistribution.  Mirrors the sequence-split and
+ * all-to-all layout state of edge-dit.cpp "Parallel execution" (original /
+ * padded / local sequence length; global / local heads; batch; head dim;
+ * elements per peer).  Fill it with dit_a2a_layout_init(); the derived
+ * fields are read-only for callers.
+ *
+ * Padding (explicit here, never hidden global state):
+ *   S_pad = ceil(S / lcm(U, seq_align)) * lcm(U, seq_align), S_loc = S_pad/U.
+ *     seq_align = 1 pads to a multiple of U (edge-dit: S divisible by the
+ *     SP degree or padded); seq_align = 64 gives xLLM's lcm(SP, 64) rule
+ *     ("DiT Architecture and Capability Matrix", MiniMax-H3 boundaries).
+ *     Pad rows are the global tail (rows >= S, on the last ranks).
+ *   H_pad = ceil(H / U) * U, H_loc = H_pad / U (cache-dit "Context
+ *     Parallelism", Any Head Num).  Pad heads are global indices >= H.
+ * Pad rows and pad heads are always written as zeros; they are never read.
+ */
+typedef struct {
+  int32_t B, S, H, D, U;  /* real sizes of the Ulysses group */
+  int32_t seq_align;      /* >= 1 */
+  int32_t n_planes;       /* 1 (one tensor) or 3 (packed Q, K, V) */
+  dit_dtype_t dtype;      /* element type; permutes are bit copies */
+  int32_t S_pad, S_loc, H_pad, H_loc; /* derived */
+  int64_t elems_per_peer;             /* derived: n_planes*B*S_loc*H_loc*D */
+} dit_a2a_layout;
+
+/* DIT_ABI_VERSION of the loaded library. */
+int dit_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* dit_status_string(dit_status_t status);
+
+/* Detail of the calling thread's last failed call ("" if none).  The
+ * pointer stays valid until the thread's next library call. */
+const char* dit_last_error(void);
+
+/*
+ * Fill *out from the real sizes.  B, S, H, D >= 0 (S or B may be 0: an empty
+ * exchange); U >= 1; seq_align >= 1; n_planes in {1, 3}; dtype any of the
+ * enum.  Errors: DIT_ERR_INVALID_ARGUMENT (out NULL, a negative size, bad
+ * U / seq_align / n_planes / dtype, or sizes whose element count overflows
+ * int64).  Host-only; touches no device.
+ */
+dit_status_t dit_a2a_layout_init(int32_t B, int32_t S, int32_t H, int32_t D, int32_t U,
+                                 int32_t seq_align, int32_t n_planes, dit_dtype_t dtype,
+                                 dit_a2a_layout* out);
+
+/*
+ * Pack the send buffer of Ulysses rank `rank` (edge-dit.cpp "Parallel
+ * execution": packed QKV operator for sequence-to-head, packed
+ * head-to-sequence operator for the inverse; SGLang "The Ulysses
+ * transport": one destination-major buffer for all planes).
+ *
+ * send_buf: [U (destination peer), n_planes, B, S_loc, H_loc, D]; the
+ *   chunk for peer p starts at element p * elems_per_peer.
+ * DIT_SEQ_TO_HEAD: in_planes[pl] is the rank's sequence shard
+ *   [B, S_loc, H, D];
+ *   send[p,pl,b,s,h',d] = in_pl[b, s, p*H_loc + h', d]
+ *   if rank*S_loc + s < S and p*H_loc + h' < H, else 0.
+ *   Rows of in_pl whose global index is >= S are never read.
+ * DIT_HEAD_TO_SEQ: in_planes[pl] is the rank's head shard [B, S, H_loc, D];
+ *   send[p,pl,b,s,h',d] = in_pl[b, p*S_loc + s, h', d]
+ *   if p*S_loc + s < S and rank*H_loc + h' < H, else 0.
+ *   Heads of in_pl whose global index is >= H are never read.
+ *
+ * in_planes is a HOST array of n_planes device pointers.  No aliasing
+ * between inputs and send_buf.  Errors: INVALID_ARGUMENT (null layout,
+ * in_planes or pointer of a non-empty tensor, bad direction, rank outside
+ * [0, U), layout fields inconsistent with dit_a2a_layout_init, overlapping
+ * tensors); UNSUPPORTED (pointer not element-aligned, exchange of 2^31 or
+ * more elements); HIP.
+ */
+dit_status_t dit_ulysses_pack(const dit_a2a_layout* layout, dit_a2a_dir_t dir, int32_t rank,
+                              const void* const* in_planes, void* send_buf, void* stream);
+
+/*
+ * Unpack the receive buffer of Ulysses rank `rank` after the all-to-all
+ * (edge-dit.cpp receive preparation without RoPE; receive-side unpack of the
+ * head-to-sequence path).  recv_buf: [U (source peer), n_planes, B, S_loc,
+ * H_loc, D]: the chunk that source peer p addressed to this rank.
+ *
+ * DIT_SEQ_TO_HEAD: out_planes[pl] is [B, S, H_loc, D] (the S real rows:
+ *   pad rows are dropped, so attention sees exactly the real keys);
+ *   out_pl[b,t,h',d] = recv[t / S_loc, pl, b, t % S_loc, h', d].
+ *   Pad heads of this rank arrive as zeros and stay zero.
+ * DIT_HEAD_TO_SEQ: out_planes[pl] is [B, S_loc, H, D] (the H real heads);
+ *   out_pl[b,s,h,d] = recv[h / H_loc, pl, b, s, h % H_loc, d] for
+ *   rank*S_loc + s < S, and 0 on this rank's pad rows.
+ *
+ * out_planes is a HOST array of n_planes device pointers.  Errors as for
+ * dit_ulysses_pack.
+ */
+dit_status_t dit_ulysses_unpack(const dit_a2a_layout* layout, dit_a2a_dir_t dir, int32_t rank,
+                                const void* recv_buf, void* const* out_planes, void* stream);
+
+/*
+ * Non-causal attention with per-row log-sum-exp (edge-dit.cpp "Parallel
+ * execution", Ulysses section: exact softmax(Q K^T / sqrt(D)) V over the
+ * full sequence of the rank's heads; SGLang "Parallelism Overview",
+ * Constraints: a ring-capable kernel must expose its softmax LSE).
+ *
+ *   s_ij   = scale * q_i . k_j
+ *   O_i    = sum_j softmax_j(s_i) v_j
+ *   LSE_i  = ln sum_j exp(s_ij)          (natural log, scale included)
+ *
+ * q: [B, Sq, H, D], k and v: [B, Skv, H, D] in in_dtype (DIT_BF16: bf16
+ *   MFMA with fp32 accumulation and fp32 softmax; DIT_F32: fp32 throughout).
+ * o: [B, Sq, H, D] in o_dtype (= in_dtype, or DIT_F32 for a bf16 input whose
+ *   output feeds an fp32 ring accumulator).
+ * lse: [B, H, Sq] fp32, or NULL when not needed.
+ * scale > 0 and finite (1/sqrt(D) for standard attention).
+ * D in {64, 128}.
+ * Sq == 0 or B == 0 or H == 0: no-op.  Skv == 0: O = 0 and LSE = -inf (the
+ *   identity of dit_attn_merge).
+ * No aliasing between inputs and outputs.  Deterministic (no atomics).
+ * Errors: INVALID_ARGUMENT (null pointer of a non-empty tensor, negative
+ * size, bad scale or dtype); UNSUPPORTED (D, dtype pair, alignment); HIP.
+ */
+dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
+                          dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* stream);
+
+/*
+ * In-place online-softmax merge of a partial result into an accumulator
+ * (SGLang "Parallelism Overview": the ring per-hop merge, also used for
+ * replicated and tail-padded parts, combines partial results with the
+ * kernel's LSE).  Per row (b, i, h), with m = max(L_acc, L_part) and
+ * w_x = exp(L_x - m):
+ *   L_acc <- m + ln(w_acc + w_part)
+ *   O_acc <- (w_acc O_acc + w_part O_part) / (w_acc + w_part)
+ * A side whose LSE is -inf is empty and is dropped (selected away, never
+ * multiplied, so its O may hold anything); both empty -> (0, -inf).
+ * Math in fp32.
+ *
+ * o_acc, o_part: [B, Sq, H, D] in o_dtype (DIT_BF16 or DIT_F32);
+ * lse_acc, lse_part: [B, H, Sq] fp32.  o_acc / lse_acc are read and
+ * written in place; they must not overlap the part tensors.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (dtype, alignment), HIP.
+ */
+dit_status_t dit_attn_merge(void* o_acc, float* lse_acc, const void* o_part,
+                            const float* lse_part, int32_t B, int32_t Sq, int32_t H, int32_t D,
+                            dit_dtype_t o_dtype, void* stream);
+
+/*
+ * Classifier-free guidance combine (edge-dit.cpp "Parallel execution", CFG
+ * parallelism section): out = p_uncond + g * (p_cond - p_uncond), evaluated
+ * per element as fmaf(g, p_cond - p_uncond, p_uncond) in fp32.
+ * p_uncond, p_cond, out: n elements of dtype (DIT_F32, or DIT_BF16 with fp32
+ * math and round-to-nearest-even output).  out may alias either input
+ * exactly (in-place); partial overlap is not allowed.  n == 0: no-op.
+ * Errors: INVALID_ARGUMENT (null pointer for n > 0, n < 0, g not finite),
+ * UNSUPPORTED (dtype, alignment), HIP.
+ */
+dit_status_t dit_cfg_combine(const void* p_uncond, const void* p_cond, void* out, int64_t n,
+                             float g, dit_dtype_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

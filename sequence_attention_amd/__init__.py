@@ -1,0 +1,175 @@
+"""Per-GPU hot path of sequence-parallel DiT attention on MI355X (gfx950).
+
+Thin Python binding over libdit_attn.so.  Every function has the name of the
+C entry point it wraps (include/dit_attn.h) and only marshals arguments:
+torch supplies device memory and the current HIP stream, all computation
+runs in the library's HIP kernels.  There is no CPU or PyTorch fallback: if
+the library is missing, or a tensor is not on the GPU, the call raises.
+
+    o, lse = dit_attn_fwd(q, k, v)                      # [B,S,H,D] bf16 / fp32
+    dit_attn_merge(o_acc, lse_acc, o_part, lse_part)    # in place
+    L = dit_a2a_layout_init(B, S, H, D, U, n_planes=3)
+    send = dit_ulysses_pack(L, DIT_SEQ_TO_HEAD, rank, [q, k, v])
+    q, k, v = dit_ulysses_unpack(L, DIT_SEQ_TO_HEAD, rank, recv)
+    out = dit_cfg_combine(p_uncond, p_cond, g)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+from ._lib import (  # noqa: F401
+    DIT_BF16, DIT_F16, DIT_F32, DIT_HEAD_TO_SEQ, DIT_OK, DIT_SEQ_TO_HEAD,
+    DIT_ERR_HIP, DIT_ERR_INVALID_ARGUMENT, DIT_ERR_UNSUPPORTED,
+    DitA2ALayout, DitError, EXPORTS, LIB_PATH, check, lib,
+)
+
+__all__ = [
+    "dit_abi_version", "dit_a2a_layout_init", "dit_ulysses_pack", "dit_ulysses_unpack",
+    "dit_attn_fwd", "dit_attn_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
+    "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return DIT_BF16
+    if dt == torch.float16:
+        return DIT_F16
+    if dt == torch.float32:
+        return DIT_F32
+    raise TypeError(f"unsupported tensor dtype {dt}")
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return {DIT_BF16: torch.bfloat16, DIT_F16: torch.float16, DIT_F32: torch.float32}[code]
+
+
+def _dev(t, name: str):
+    """Device pointer of a contiguous GPU tensor."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def dit_abi_version() -> int:
+    return lib().dit_abi_version()
+
+
+def dit_a2a_layout_init(B, S, H, D, U, seq_align=1, n_planes=1, dtype=DIT_BF16) -> DitA2ALayout:
+    """Derived sizes of one Ulysses redistribution (host only)."""
+    if not isinstance(dtype, int):
+        dtype = _dtype_code(dtype)
+    L = DitA2ALayout()
+    check(lib().dit_a2a_layout_init(B, S, H, D, U, seq_align, n_planes, dtype, ctypes.byref(L)),
+          "dit_a2a_layout_init")
+    return L
+
+
+def _send_shape(L):
+    return (L.U, L.n_planes, L.B, L.S_loc, L.H_loc, L.D)
+
+
+def dit_ulysses_pack(layout: DitA2ALayout, direction: int, rank: int, planes, send=None,
+                     stream=None):
+    """Pack rank `rank`'s planes into a peer-major send buffer
+    [U, n_planes, B, S_loc, H_loc, D] (allocated if `send` is None)."""
+    torch = _torch()
+    planes = list(planes)
+    if len(planes) != layout.n_planes:
+        raise ValueError(f"expected {layout.n_planes} planes, got {len(planes)}")
+    if send is None:
+        send = torch.empty(_send_shape(layout), dtype=_torch_dtype(layout.dtype),
+                           device=planes[0].device)
+    arr = (ctypes.c_void_p * 3)(*[_dev(p, f"planes[{i}]") for i, p in enumerate(planes)])
+    check(lib().dit_ulysses_pack(ctypes.byref(layout), direction, rank, arr, _dev(send, "send"),
+                                 _stream(stream)), "dit_ulysses_pack")
+    return send
+
+
+def dit_ulysses_unpack(layout: DitA2ALayout, direction: int, rank: int, recv, out=None,
+                       stream=None):
+    """Unpack a receive buffer into n_planes tensors: [B, S, H_loc, D] for
+    DIT_SEQ_TO_HEAD, [B, S_loc, H, D] for DIT_HEAD_TO_SEQ."""
+    torch = _torch()
+    if out is None:
+        shape = ((layout.B, layout.S, layout.H_loc, layout.D) if direction == DIT_SEQ_TO_HEAD
+                 else (layout.B, layout.S_loc, layout.H, layout.D))
+        out = [torch.empty(shape, dtype=_torch_dtype(layout.dtype), device=recv.device)
+               for _ in range(layout.n_planes)]
+    out = list(out)
+    arr = (ctypes.c_void_p * 3)(*[_dev(p, f"out[{i}]") for i, p in enumerate(out)])
+    check(lib().dit_ulysses_unpack(ctypes.byref(layout), direction, rank, _dev(recv, "recv"), arr,
+                                   _stream(stream)), "dit_ulysses_unpack")
+    return out
+
+
+def dit_attn_fwd(q, k, v, o=None, lse=None, scale=None, o_dtype=None, want_lse=True,
+                 stream=None):
+    """Attention over [B, S, H, D] tensors; returns (O, LSE) with LSE
+    [B, H, Sq] fp32 (None if want_lse is False and no buffer was given)."""
+    torch = _torch()
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if tuple(k.shape) != (B, Skv, H, D) or tuple(v.shape) != (B, Skv, H, D):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    in_code = _dtype_code(q.dtype)
+    if o is None:
+        o = torch.empty((B, Sq, H, D), dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    lse_ptr = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
+    check(lib().dit_attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lse_ptr,
+                             B, Sq, Skv, H, D, float(scale), in_code, _dtype_code(o.dtype),
+                             _stream(stream)), "dit_attn_fwd")
+    return o, lse
+
+
+def dit_attn_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
+    """In-place merge of (o_part, lse_part) into (o_acc, lse_acc)."""
+    B, Sq, H, D = o_acc.shape
+    if tuple(o_part.shape) != (B, Sq, H, D) or o_part.dtype != o_acc.dtype:
+        raise ValueError("o_part must match o_acc in shape and dtype")
+    if tuple(lse_acc.shape) != (B, H, Sq) or tuple(lse_part.shape) != (B, H, Sq):
+        raise ValueError(f"LSE tensors must be [B, H, Sq] = {(B, H, Sq)}")
+    check(lib().dit_attn_merge(_dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc"), _dev(o_part, "o_part"),
+                               _dev(lse_part, "lse_part"), B, Sq, H, D, _dtype_code(o_acc.dtype),
+                               _stream(stream)), "dit_attn_merge")
+    return o_acc, lse_acc
+
+
+def dit_cfg_combine(p_uncond, p_cond, g: float, out=None, stream=None):
+    """out = p_uncond + g * (p_cond - p_uncond) elementwise (out may be an input)."""
+    torch = _torch()
+    if p_cond.shape != p_uncond.shape or p_cond.dtype != p_uncond.dtype:
+        raise ValueError("p_cond must match p_uncond in shape and dtype")
+    if out is None:
+        out = torch.empty_like(p_uncond)
+    elif out.shape != p_uncond.shape or out.dtype != p_uncond.dtype:
+        raise ValueError("out must match p_uncond in shape and dtype")
+    check(lib().dit_cfg_combine(_dev(p_uncond, "p_uncond"), _dev(p_cond, "p_cond"), _dev(out, "out"),
+                                p_uncond.numel(), float(g), _dtype_code(p_uncond.dtype),
+                                _stream(stream)), "dit_cfg_combine")
+    return out

@@ -1,0 +1,79 @@
+// Internal launch interface between the C-ABI layer (dit_abi.cpp) and the
+// gfx950 kernels.  Every launcher assumes its arguments were validated by
+// the ABI layer (sizes, alignment, dtype) and only enqueues work on
+// `stream`; it returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+// Division by a run-time constant n / d for 0 <= n < 2^31, 1 <= d < 2^31
+// (round-up multiplier method, Granlund and Montgomery 1994):
+//   s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1,
+//   n / d = (mulhi(n, m) + n) >> s.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.s = s;
+  f.m = (uint32_t)((((1ull << s) - d) << 32) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// ---- Ulysses permutes -------------------------------------------------------
+enum PermuteKind : int {
+  PACK_SEQ_TO_HEAD = 0,
+  UNPACK_SEQ_TO_HEAD = 1,
+  PACK_HEAD_TO_SEQ = 2,
+  UNPACK_HEAD_TO_SEQ = 3,
+};
+
+struct PermuteArgs {
+  const void* in[3];   // PACK: planes; UNPACK: in[0] = receive buffer
+  void* out[3];        // PACK: out[0] = send buffer; UNPACK: planes
+  int32_t B, S, H, D, U, n_planes, S_loc, H_loc, rank;
+  int32_t elem_bytes;
+};
+
+hipError_t launch_permute(PermuteKind kind, const PermuteArgs& a, hipStream_t stream);
+
+// ---- CFG combine ------------------------------------------------------------
+hipError_t launch_cfg_combine_f32(const float* u, const float* c, float* out, int64_t n, float g,
+                                  hipStream_t stream);
+hipError_t launch_cfg_combine_bf16(const uint16_t* u, const uint16_t* c, uint16_t* out, int64_t n,
+                                   float g, hipStream_t stream);
+
+// ---- merge -------------------------------------------------------------------
+hipError_t launch_attn_merge(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part,
+                             int32_t B, int32_t Sq, int32_t H, int32_t D, bool o_f32,
+                             hipStream_t stream);
+
+// ---- attention ---------------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int32_t B, Sq, Skv, H, D;
+  float scale;
+  bool o_f32;  // bf16 input only: write O as fp32
+};
+
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
+// Skv == 0: O = 0, LSE = -inf.
+hipError_t launch_attn_empty(const AttnArgs& a, bool in_f32, hipStream_t stream);
+
+}  // namespace dit

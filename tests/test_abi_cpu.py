@@ -1,0 +1,210 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, derives Ulysses layouts like the oracle, and
+rejects every invalid call with its status code before any HIP call (fake,
+never dereferenced device addresses stand in for tensors)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+import sequence_attention_amd as sa
+from sequence_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_attn.h")
+
+INV = sa.DIT_ERR_INVALID_ARGUMENT
+UNS = sa.DIT_ERR_UNSUPPORTED
+P = ctypes.c_void_p
+A = 0x7f0000000000          # fake, 256-byte aligned device address
+NULL = P(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from sequence_attention_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_is_plain_c():
+    text = open(HEADER).read()
+    assert "#include <stdint.h>" in text
+    code = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    assert re.findall(r"#include\s*[<\"]([^>\"]+)", code) == ["stdint.h"]
+    assert "hipStream_t" not in code
+    assert "torch" not in text.lower()
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dit_abi_version() == 1
+    for code, name in [(0, "DIT_OK"), (1, "DIT_ERR_INVALID_ARGUMENT"), (2, "DIT_ERR_UNSUPPORTED"),
+                       (3, "DIT_ERR_HIP")]:
+        assert lib.dit_status_string(code).decode() == name
+    assert lib.dit_status_string(42)
+
+
+@pytest.mark.parametrize("args", [
+    (1, 256, 4, 64, 2, 1, 3), (1, 4608, 24, 128, 2, 1, 3), (2, 7145, 24, 128, 4, 1, 3),
+    (2, 7145, 24, 128, 5, 1, 3), (2, 7145, 24, 128, 4, 64, 1), (1, 75600, 40, 128, 8, 1, 1),
+    (3, 10, 7, 8, 3, 4, 1), (1, 0, 4, 8, 2, 1, 1), (0, 5, 3, 8, 4, 1, 3), (1, 3, 4, 2, 4, 1, 1),
+])
+def test_layout_matches_oracle(lib, args):
+    L = sa.dit_a2a_layout_init(*args)
+    want = oracle.a2a_layout(*args)
+    for key in ("S_pad", "S_loc", "H_pad", "H_loc", "elems_per_peer"):
+        assert getattr(L, key) == want[key], key
+
+
+def _layout(lib, *args):
+    L = _lib.DitA2ALayout()
+    assert lib.dit_a2a_layout_init(*args, ctypes.byref(L)) == 0
+    return L
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 8, 4, 8, 2, 1, 1, 0), INV),
+    ((1, -8, 4, 8, 2, 1, 1, 0), INV),
+    ((1, 8, 4, -8, 2, 1, 1, 0), INV),
+    ((1, 8, 4, 8, 0, 1, 1, 0), INV),
+    ((1, 8, 4, 8, 2, 0, 1, 0), INV),
+    ((1, 8, 4, 8, 2, 1, 2, 0), INV),
+    ((1, 8, 4, 8, 2, 1, 1, 9), INV),
+    ((2**30, 2**30, 4, 2**30, 1, 1, 3, 0), INV),
+])
+def test_layout_init_rejects(lib, args, code):
+    L = _lib.DitA2ALayout()
+    assert lib.dit_a2a_layout_init(*args, ctypes.byref(L)) == code
+    assert lib.dit_last_error().decode() != ""
+
+
+def test_layout_init_null_out(lib):
+    assert lib.dit_a2a_layout_init(1, 8, 4, 8, 2, 1, 1, 0, None) == INV
+
+
+def _planes(*ptrs):
+    return (P * 3)(*[P(p) for p in ptrs])
+
+
+def test_pack_unpack_rejects(lib):
+    L = _layout(lib, 1, 8, 4, 8, 2, 1, 3, 0)
+    ok3 = _planes(A, A + 4096, A + 8192)
+    send = P(A + 65536)
+    pack, unpack = lib.dit_ulysses_pack, lib.dit_ulysses_unpack
+    assert pack(None, 0, 0, ok3, send, NULL) == INV
+    assert pack(ctypes.byref(L), 2, 0, ok3, send, NULL) == INV           # direction
+    assert pack(ctypes.byref(L), 0, -1, ok3, send, NULL) == INV          # rank
+    assert pack(ctypes.byref(L), 0, 2, ok3, send, NULL) == INV           # rank == U
+    assert pack(ctypes.byref(L), 0, 0, None, send, NULL) == INV          # plane array
+    assert pack(ctypes.byref(L), 0, 0, _planes(A, 0, A + 8192), send, NULL) == INV
+    assert pack(ctypes.byref(L), 0, 0, ok3, NULL, NULL) == INV           # send buffer
+    assert pack(ctypes.byref(L), 0, 0, _planes(A + 1, A + 4096, A + 8192), send, NULL) == UNS
+    assert pack(ctypes.byref(L), 0, 0, ok3, P(A + 4096), NULL) == INV    # overlap
+    assert "overlap" in lib.dit_last_error().decode()
+    assert unpack(ctypes.byref(L), 0, 0, NULL, ok3, NULL) == INV         # recv NULL
+    assert unpack(ctypes.byref(L), 1, 0, send, _planes(A, A, A + 8192), NULL) == INV  # outputs overlap
+    assert unpack(ctypes.byref(L), 0, 0, send, None, NULL) == INV
+    bad = _lib.DitA2ALayout.from_buffer_copy(L)
+    bad.S_loc += 1                                                        # tampered derived field
+    assert pack(ctypes.byref(bad), 0, 0, ok3, send, NULL) == INV
+    assert "derived" in lib.dit_last_error().decode()
+    huge = _layout(lib, 1, 2**21, 1024, 128, 2, 1, 3, 0)                  # >= 2^31 elements
+    assert pack(ctypes.byref(huge), 0, 0, ok3, send, NULL) == UNS
+
+
+def test_empty_exchange_is_a_no_op(lib):
+    L = _layout(lib, 0, 8, 4, 8, 2, 1, 3, 0)
+    assert lib.dit_ulysses_pack(ctypes.byref(L), 0, 0, _planes(0, 0, 0), NULL, NULL) == 0
+    assert lib.dit_ulysses_unpack(ctypes.byref(L), 1, 1, NULL, _planes(0, 0, 0), NULL) == 0
+
+
+def _attn(lib, q=A, k=A + 2**24, v=A + 2**25, o=A + 2**26, lse=A + 2**27, B=1, Sq=128, Skv=128,
+          H=2, D=64, scale=0.125, din=0, dout=0):
+    return lib.dit_attn_fwd(P(q), P(k), P(v), P(o), P(lse), B, Sq, Skv, H, D, scale, din, dout, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), INV), (dict(Sq=-1), INV), (dict(Skv=-5), INV), (dict(H=-1), INV),
+    (dict(din=7), INV), (dict(dout=5), INV),
+    (dict(scale=0.0), INV), (dict(scale=-1.0), INV), (dict(scale=math.nan), INV),
+    (dict(scale=math.inf), INV),
+    (dict(din=1, dout=1), UNS),                     # fp16 not served
+    (dict(D=96), UNS), (dict(D=256), UNS),
+    (dict(din=0, dout=1), UNS), (dict(din=2, dout=0), UNS),
+    (dict(q=0), INV), (dict(o=0), INV), (dict(k=0), INV), (dict(v=0), INV),
+    (dict(q=A + 8), UNS), (dict(k=A + 2**24 + 2), UNS), (dict(o=A + 2**26 + 4), UNS),
+    (dict(lse=A + 2**27 + 2), UNS),
+    (dict(o=A + 1024), INV),                        # o overlaps q
+    (dict(lse=A + 2**26 + 64), INV),                # lse overlaps o
+])
+def test_attn_rejects(lib, kw, code):
+    assert _attn(lib, **kw) == code, lib.dit_last_error()
+    assert lib.dit_last_error().decode() != ""
+
+
+def test_attn_empty_is_a_no_op(lib):
+    assert _attn(lib, q=0, k=0, v=0, o=0, lse=0, Sq=0) == 0
+    assert _attn(lib, q=0, k=0, v=0, o=0, lse=0, B=0) == 0
+    assert _attn(lib, q=0, k=0, v=0, o=0, lse=0, H=0) == 0
+    assert lib.dit_last_error().decode() == ""
+
+
+def _merge(lib, oa=A, la=A + 2**24, op=A + 2**25, lp=A + 2**26, B=1, Sq=16, H=2, D=64, dt=0):
+    return lib.dit_attn_merge(P(oa), P(la), P(op), P(lp), B, Sq, H, D, dt, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), INV), (dict(D=-8), INV), (dict(dt=9), INV), (dict(dt=1), UNS),
+    (dict(D=96), UNS), (dict(D=12), UNS), (dict(D=1024), UNS),
+    (dict(oa=0), INV), (dict(lp=0), INV),
+    (dict(oa=A + 8), UNS), (dict(la=A + 2**24 + 2), UNS),
+    (dict(op=A + 256), INV), (dict(lp=A + 2**24 + 4), INV),
+])
+def test_merge_rejects(lib, kw, code):
+    assert _merge(lib, **kw) == code
+
+
+def test_merge_empty_is_a_no_op(lib):
+    assert _merge(lib, oa=0, la=0, op=0, lp=0, Sq=0) == 0
+
+
+def _cfg(lib, u=A, c=A + 2**20, out=A + 2**21, n=1000, g=4.0, dt=2):
+    return lib.dit_cfg_combine(P(u), P(c), P(out), n, g, dt, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), INV), (dict(g=math.inf), INV), (dict(g=math.nan), INV), (dict(dt=4), INV),
+    (dict(dt=1), UNS), (dict(u=0), INV), (dict(out=0), INV),
+    (dict(u=A + 4), UNS), (dict(out=A + 16), INV),  # partial overlap with u
+])
+def test_cfg_rejects(lib, kw, code):
+    assert _cfg(lib, **kw) == code
+
+
+def test_cfg_empty_is_a_no_op(lib):
+    assert _cfg(lib, u=0, c=0, out=0, n=0) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sa.dit_attn_fwd(q, q, q, o=q.clone(), lse=torch.zeros(1, 1, 4))

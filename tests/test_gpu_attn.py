@@ -1,0 +1,197 @@
+"""GPU parity of dit_attn_fwd (bf16 MFMA path and fp32 path) against the
+fp64 oracle, on the workload shapes, ragged tails, stress inputs and the
+closed forms.
+
+Tolerances (max-abs against the fp64 oracle): bf16 O <= 1e-2 and
+LSE <= 1e-3; fp32 O and LSE <= 1e-5.  Because |O| is far below 1e-2 at
+long sequences, every bf16 case also bounds max|dO| / max|O| <= 2e-2 (bf16
+rounding of P and of O is ~2^-9 relative each).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sequence_attention_amd as sa
+from sequence_attention_amd import workloads
+from tests.gpu_util import DEV, Guarded, log, max_abs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: (1e-2, 1e-3), torch.float32: (1e-5, 1e-5)}
+REL_BF16 = 2e-2
+
+
+def run_attn(q, k, v, scale=None, o_dtype=None, lse=True):
+    B, Sq, H, D = q.shape
+    od = o_dtype or q.dtype
+    o = Guarded((B, Sq, H, D), od, fill_bits=0x7FC0 if od == torch.bfloat16 else 0x7FC00000)
+    l = Guarded((B, H, Sq), torch.float32, fill_bits=0x7FC00000) if lse else None
+    sa.dit_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), o=o.t, lse=l.t if lse else None, scale=scale)
+    torch.cuda.synchronize()
+    assert o.canary_ok(), "write past the end of O"
+    if lse:
+        assert l.canary_ok(), "write past the end of LSE"
+    return o.t, (l.t if lse else None)
+
+
+def check(o, lse, q, k, v, scale, rows=None, dtype=torch.bfloat16, what=""):
+    ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), scale, rows=rows)
+    go = o.float().cpu().numpy()
+    gl = lse.cpu().numpy() if lse is not None else None
+    if rows is not None:
+        go = go[:, rows]
+        gl = gl[:, :, rows] if gl is not None else None
+    tol_o, tol_l = TOL[dtype]
+    eo = max_abs(go, ro)
+    assert np.all(np.isfinite(go)), f"{what}: non-finite O"
+    assert eo <= tol_o, f"{what}: O max-abs {eo:.3e} > {tol_o}"
+    if dtype == torch.bfloat16:
+        rel = eo / max(np.max(np.abs(ro)), 1e-30)
+        assert rel <= REL_BF16, f"{what}: O relative {rel:.3e} > {REL_BF16}"
+    if gl is not None:
+        el = max_abs(gl, rl)
+        assert el <= tol_l, f"{what}: LSE max-abs {el:.3e} > {tol_l}"
+    return eo
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux", "qwen_u4"])
+def test_workload_full_parity(name):
+    w = workloads.WORKLOADS[name]
+    log(f"attn bf16 full parity {name}")
+    q, k, v = workloads.attention_inputs(w)
+    o, lse = run_attn(q, k, v, w.scale)
+    check(o, lse, q, k, v, w.scale, what=name)
+
+
+def test_qwen_u5_pad_head_closed_form_and_parity():
+    w = workloads.WORKLOADS["qwen_u5"]
+    log("attn bf16 qwen_u5 with a zero pad head")
+    q, k, v = workloads.attention_inputs(w)
+    # the last rank's 5th head is the pad head: zeros after the exchange
+    for t in (q, k, v):
+        t[:, :, 4] = 0
+    o, lse = run_attn(q, k, v, w.scale)
+    assert torch.count_nonzero(o[:, :, 4]).item() == 0
+    np.testing.assert_allclose(lse[:, 4].cpu().numpy(), math.log(w.Skv), atol=1e-3)
+    check(o, lse, q, k, v, w.scale, what="qwen_u5")
+
+
+def test_ring_shard_unchunked_sampled_rows():
+    w = workloads.WORKLOADS["ring"]
+    log("attn bf16 ring shard unchunked [1,4096,24,128] x 16384")
+    q, k, v = workloads.attention_inputs(w)
+    o, lse = run_attn(q, k, v, w.scale)
+    rows = np.unique(np.concatenate([np.arange(0, 4096, 97), [4095]]))
+    check(o, lse, q, k, v, w.scale, rows=rows, what="ring unchunked")
+
+
+def test_wan_sampled_rows():
+    w = workloads.WORKLOADS["wan"]
+    log("attn bf16 wan [1,75600,5,128] sampled rows")
+    q, k, v = workloads.attention_inputs(w)
+    o, lse = run_attn(q, k, v, w.scale)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([rng.choice(75600, 160, replace=False),
+                                     [0, 1, 127, 128, 75599, 75600 - 80]]))
+    check(o, lse, q, k, v, w.scale, rows=rows, what="wan")
+
+
+def test_q_zero_closed_form_at_flux_size():
+    w = workloads.WORKLOADS["flux"]
+    log("attn bf16 flux Q=0 closed form")
+    q, k, v = workloads.attention_inputs(w, stress="qzero")
+    o, lse = run_attn(q, k, v, w.scale)
+    mean_v = v.double().mean(dim=1, keepdim=True).expand_as(v).numpy()
+    assert max_abs(o.float().cpu().numpy(), mean_v) <= 1e-2
+    np.testing.assert_allclose(lse.cpu().numpy(), math.log(w.Skv), atol=1e-3)
+
+
+@pytest.mark.parametrize("stress", ["sharp", "vmean1", "huge", "qzero"])
+@pytest.mark.parametrize("name", ["tiny", "flux"])
+def test_stress_inputs(name, stress):
+    w = workloads.WORKLOADS[name]
+    log(f"attn bf16 stress {stress} {name}")
+    q, k, v = workloads.attention_inputs(w, stress=stress, seed=3)
+    o, lse = run_attn(q, k, v, w.scale)
+    rows = None if name == "tiny" else np.arange(0, w.Sq, 7)
+    check(o, lse, q, k, v, w.scale, rows=rows, what=f"{name}/{stress}")
+
+
+RAGGED = [
+    # B, Sq, Skv, H, D
+    (1, 1, 1, 1, 64), (1, 1, 1, 1, 128), (1, 7, 5, 2, 128), (2, 130, 65, 3, 64),
+    (1, 129, 1000, 2, 128), (3, 200, 129, 1, 64), (1, 256, 64, 4, 128), (1, 33, 4097, 1, 128),
+    (2, 1, 300, 5, 128),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_ragged_shapes(shape, dtype):
+    B, Sq, Skv, H, D = shape
+    log(f"attn {dtype} ragged {shape}")
+    w = workloads.Workload("ragged", B=B, Sq=Sq, Skv=Skv, H=H, D=D, R=1, S=Skv, H_total=H, U=1)
+    q, k, v = workloads.attention_inputs(w, dtype=dtype, seed=sum(shape))
+    o, lse = run_attn(q, k, v, w.scale)
+    check(o, lse, q, k, v, w.scale, dtype=dtype, what=f"{shape}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux"])
+def test_fp32_path(name):
+    w = workloads.WORKLOADS[name]
+    log(f"attn fp32 {name}")
+    q, k, v = workloads.attention_inputs(w, dtype=torch.float32)
+    o, lse = run_attn(q, k, v, w.scale)
+    rows = None if name == "tiny" else np.arange(0, w.Sq, 11)
+    check(o, lse, q, k, v, w.scale, rows=rows, dtype=torch.float32, what=f"fp32 {name}")
+
+
+def test_bf16_in_fp32_out():
+    w = workloads.WORKLOADS["tiny"]
+    log("attn bf16 in, fp32 out")
+    q, k, v = workloads.attention_inputs(w)
+    o, lse = run_attn(q, k, v, w.scale, o_dtype=torch.float32)
+    assert o.dtype == torch.float32
+    check(o, lse, q, k, v, w.scale, what="bf16->fp32")
+    o16, lse16 = run_attn(q, k, v, w.scale)
+    # the bf16 output is the fp32 output rounded to nearest even
+    assert torch.equal(o16.cpu(), o.cpu().to(torch.bfloat16))
+    assert torch.equal(lse16.cpu(), lse.cpu())
+
+
+def test_empty_keys_give_merge_identity():
+    log("attn Skv=0")
+    q = torch.randn(1, 70, 3, 128).to(torch.bfloat16)
+    k = torch.zeros(1, 0, 3, 128, dtype=torch.bfloat16)
+    o, lse = run_attn(q, k, k, 0.1)
+    assert torch.count_nonzero(o).item() == 0
+    assert torch.isneginf(lse).all().item()
+
+
+def test_no_lse_buffer():
+    w = workloads.WORKLOADS["tiny"]
+    q, k, v = workloads.attention_inputs(w)
+    o, _ = run_attn(q, k, v, w.scale, lse=False)
+    o2, _ = run_attn(q, k, v, w.scale)
+    assert torch.equal(o.cpu(), o2.cpu())
+
+
+def test_run_twice_is_bitwise_identical():
+    w = workloads.WORKLOADS["flux"]
+    log("attn determinism flux")
+    q, k, v = (t.to(DEV) for t in workloads.attention_inputs(w))
+    o1, l1 = sa.dit_attn_fwd(q, k, v)
+    o2, l2 = sa.dit_attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_custom_scale():
+    w = workloads.WORKLOADS["tiny"]
+    q, k, v = workloads.attention_inputs(w, seed=9)
+    o, lse = run_attn(q, k, v, 0.37)
+    check(o, lse, q, k, v, 0.37, what="scale 0.37")

@@ -1,0 +1,181 @@
+"""GPU parity of the Ulysses pack / unpack permutations (bit-exact).
+
+Small and ragged cases simulate every rank of the Ulysses group on the one
+GPU (pack on each rank, the exchange as a device chunk transpose, unpack on
+each rank) and compare with the oracle's composition.  The full workload
+sizes (FLUX, Qwen with sequence and head padding, Wan) compare single ranks
+against the oracle's index maps, element for element, on raw bit patterns.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sequence_attention_amd as sa
+from sequence_attention_amd import workloads
+from tests.gpu_util import DEV, Guarded, bits, log, simulate_all_to_all
+
+pytestmark = pytest.mark.gpu
+
+S2H, H2S = sa.DIT_SEQ_TO_HEAD, sa.DIT_HEAD_TO_SEQ
+GARBAGE = -21846  # 0xAAAA: fills pad rows / heads of inputs that must never be read
+
+
+def _layout(B, S, H, D, U, al, n, dtype=torch.bfloat16):
+    L = sa.dit_a2a_layout_init(B, S, H, D, U, al, n, dtype)
+    return L, oracle.a2a_layout(B, S, H, D, U, al, n)
+
+
+def _rand(shape, seed, dtype=torch.bfloat16):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=g).to(dtype)
+
+
+def _np_bits(t):
+    return bits(t)
+
+
+SMALL = [
+    # B, S, H, D, U, seq_align, n_planes, dtype
+    (1, 256, 4, 64, 2, 1, 3, torch.bfloat16),     # tiny config, packed QKV
+    (1, 256, 4, 64, 2, 1, 1, torch.bfloat16),     # tiny config, O
+    (2, 37, 5, 8, 3, 1, 3, torch.bfloat16),       # ragged S and H
+    (1, 10, 6, 4, 4, 1, 1, torch.float32),        # fp32, S and H padded
+    (2, 9, 3, 16, 2, 4, 3, torch.bfloat16),       # seq_align 4
+    (1, 5, 2, 6, 5, 1, 1, torch.bfloat16),        # U > H, odd D (2-byte vectors)
+    (1, 3, 4, 2, 4, 1, 1, torch.float32),         # a rank with only pad rows
+    (2, 101, 7, 24, 3, 64, 3, torch.bfloat16),    # lcm(3, 64) alignment
+]
+
+
+@pytest.mark.parametrize("case", SMALL)
+def test_all_ranks_round_trip_matches_oracle(case):
+    B, S, H, D, U, al, n, dt = case
+    log(f"permute all-ranks {case}")
+    L, Lo = _layout(B, S, H, D, U, al, n, dt)
+    glob = [_rand((B, S, H, D), 100 + pl, dt) for pl in range(n)]
+    # sequence shards with garbage in the pad rows
+    shards = []
+    for r in range(U):
+        planes = []
+        for pl in range(n):
+            x = torch.full((B, L.S_loc, H, D), 0, dtype=dt)
+            x.view(torch.int16 if dt == torch.bfloat16 else torch.int32).fill_(GARBAGE)
+            lo, hi = r * L.S_loc, min(S, (r + 1) * L.S_loc)
+            if hi > lo:
+                x[:, : hi - lo] = glob[pl][:, lo:hi]
+            planes.append(x)
+        shards.append(planes)
+
+    sends = []
+    for r in range(U):
+        send = Guarded((U, n, B, L.S_loc, L.H_loc, D), dt)
+        sa.dit_ulysses_pack(L, S2H, r, [p.to(DEV) for p in shards[r]], send=send.t)
+        torch.cuda.synchronize()
+        assert send.canary_ok()
+        want = oracle.pack_seq_to_head([_np_bits(p) for p in shards[r]], Lo, r)
+        np.testing.assert_array_equal(_np_bits(send.t), want)
+        sends.append(send.t)
+    recvs = simulate_all_to_all(sends)
+    heads = []
+    for r in range(U):
+        outs = [Guarded((B, S, L.H_loc, D), dt, fill_bits=GARBAGE) for _ in range(n)]
+        sa.dit_ulysses_unpack(L, S2H, r, recvs[r], out=[o.t for o in outs])
+        torch.cuda.synchronize()
+        assert all(o.canary_ok() for o in outs)
+        want = oracle.unpack_seq_to_head(_np_bits(recvs[r]), Lo, r)
+        for pl in range(n):
+            np.testing.assert_array_equal(_np_bits(outs[pl].t), want[pl])
+            # end to end: rank r holds heads r*H_loc.. of the global tensor
+            gl = glob[pl]
+            for hh in range(L.H_loc):
+                gh = r * L.H_loc + hh
+                ref = gl[:, :, gh] if gh < H else torch.zeros_like(gl[:, :, 0])
+                assert torch.equal(outs[pl].t[:, :, hh].cpu(), ref)
+        heads.append([o.t for o in outs])
+
+    # inverse direction: garbage in the pad heads of the head shards
+    sends = []
+    for r in range(U):
+        planes = []
+        for pl in range(n):
+            x = heads[r][pl].clone()
+            for hh in range(L.H_loc):
+                if r * L.H_loc + hh >= H:
+                    x[:, :, hh].view(torch.int16 if dt == torch.bfloat16 else torch.int32).fill_(GARBAGE)
+            planes.append(x)
+        send = Guarded((U, n, B, L.S_loc, L.H_loc, D), dt)
+        sa.dit_ulysses_pack(L, H2S, r, planes, send=send.t)
+        torch.cuda.synchronize()
+        assert send.canary_ok()
+        want = oracle.pack_head_to_seq([_np_bits(p) for p in planes], Lo, r)
+        np.testing.assert_array_equal(_np_bits(send.t), want)
+        sends.append(send.t)
+    recvs = simulate_all_to_all(sends)
+    for r in range(U):
+        outs = [Guarded((B, L.S_loc, H, D), dt, fill_bits=GARBAGE) for _ in range(n)]
+        sa.dit_ulysses_unpack(L, H2S, r, recvs[r], out=[o.t for o in outs])
+        torch.cuda.synchronize()
+        assert all(o.canary_ok() for o in outs)
+        want = oracle.unpack_head_to_seq(_np_bits(recvs[r]), Lo, r)
+        for pl in range(n):
+            np.testing.assert_array_equal(_np_bits(outs[pl].t), want[pl])
+            # the round trip restores the shard, with zeros in its pad rows
+            ref = shards[r][pl].clone()
+            for s in range(L.S_loc):
+                if r * L.S_loc + s >= S:
+                    ref[:, s] = 0
+            np.testing.assert_array_equal(_np_bits(outs[pl].t), _np_bits(ref))
+
+
+FULL = [
+    # name, B, S, H, D, U, seq_align, n_planes, ranks
+    ("flux-qkv", 1, 4608, 24, 128, 2, 1, 3, [0, 1]),
+    ("qwen-u4-qkv", 2, 7145, 24, 128, 4, 1, 3, [0, 3]),      # last rank: 3 pad rows
+    ("qwen-u4-align64", 2, 7145, 24, 128, 4, 64, 1, [3]),
+    ("qwen-u5-qkv", 2, 7145, 24, 128, 5, 1, 3, [0, 4]),      # last rank: a pad head
+    ("wan-o", 1, 75600, 40, 128, 8, 1, 1, [0, 7]),
+    ("wan-qkv", 1, 75600, 40, 128, 8, 1, 3, [5]),
+]
+
+
+@pytest.mark.parametrize("case", FULL, ids=[c[0] for c in FULL])
+def test_full_size_single_ranks_match_oracle(case):
+    name, B, S, H, D, U, al, n, ranks = case
+    L, Lo = _layout(B, S, H, D, U, al, n)
+    for r in ranks:
+        log(f"permute full {name} rank {r}: pack/unpack both directions")
+        shard = [_rand((B, L.S_loc, H, D), 10 * r + pl) for pl in range(n)]
+        send = sa.dit_ulysses_pack(L, S2H, r, [x.to(DEV) for x in shard])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_np_bits(send), oracle.pack_seq_to_head(
+            [_np_bits(x) for x in shard], Lo, r))
+        del send
+        recv = _rand((U, n, B, L.S_loc, L.H_loc, D), 77 + r)
+        outs = sa.dit_ulysses_unpack(L, S2H, r, recv.to(DEV))
+        torch.cuda.synchronize()
+        want = oracle.unpack_seq_to_head(_np_bits(recv), Lo, r)
+        for pl in range(n):
+            np.testing.assert_array_equal(_np_bits(outs[pl]), want[pl])
+        del outs
+        heads = [_rand((B, S, L.H_loc, D), 55 + pl) for pl in range(n)]
+        send = sa.dit_ulysses_pack(L, H2S, r, [x.to(DEV) for x in heads])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_np_bits(send), oracle.pack_head_to_seq(
+            [_np_bits(x) for x in heads], Lo, r))
+        del send
+        outs = sa.dit_ulysses_unpack(L, H2S, r, recv.to(DEV))
+        torch.cuda.synchronize()
+        want = oracle.unpack_head_to_seq(_np_bits(recv), Lo, r)
+        for pl in range(n):
+            np.testing.assert_array_equal(_np_bits(outs[pl]), want[pl])
+
+
+def test_run_twice_is_bitwise_identical():
+    L, _ = _layout(1, 4608, 24, 128, 2, 1, 3)
+    shard = [_rand((1, L.S_loc, 24, 128), pl).to(DEV) for pl in range(3)]
+    a = sa.dit_ulysses_pack(L, S2H, 1, shard)
+    b = sa.dit_ulysses_pack(L, S2H, 1, shard)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
