@@ -6,6 +6,12 @@ Tolerances (max-abs against the fp64 oracle): bf16 O <= 1e-2 and
 LSE <= 1e-3; fp32 O and LSE <= 1e-5.  Because |O| is far below 1e-2 at
 long sequences, every bf16 case also bounds max|dO| / max|O| <= 2e-2 (bf16
 rounding of P and of O is ~2^-9 relative each).
+
+Stress inputs whose outputs reach |O| >= 2.56 ("sharp": near one-hot
+softmax picks single V rows) cannot meet an absolute 1e-2 in any bf16
+output: storing O alone costs half an ulp, 2^-8 |O|.  There the bound is
+1e-2 + 2^-8 |O_ref| per element (the stored-output rounding added to the
+absolute bound); the relative and LSE bounds are unchanged.
 """
 
 import math
@@ -38,7 +44,7 @@ def run_attn(q, k, v, scale=None, o_dtype=None, lse=True):
     return o.t, (l.t if lse else None)
 
 
-def check(o, lse, q, k, v, scale, rows=None, dtype=torch.bfloat16, what=""):
+def check(o, lse, q, k, v, scale, rows=None, dtype=torch.bfloat16, what="", out_rounding=False):
     ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), scale, rows=rows)
     go = o.float().cpu().numpy()
     gl = lse.cpu().numpy() if lse is not None else None
@@ -48,7 +54,11 @@ def check(o, lse, q, k, v, scale, rows=None, dtype=torch.bfloat16, what=""):
     tol_o, tol_l = TOL[dtype]
     eo = max_abs(go, ro)
     assert np.all(np.isfinite(go)), f"{what}: non-finite O"
-    assert eo <= tol_o, f"{what}: O max-abs {eo:.3e} > {tol_o}"
+    if out_rounding:
+        excess = np.max(np.abs(go - ro) - (tol_o + 2.0 ** -8 * np.abs(ro)))
+        assert excess <= 0, f"{what}: O error exceeds 1e-2 + 2^-8|O| by {excess:.3e}"
+    else:
+        assert eo <= tol_o, f"{what}: O max-abs {eo:.3e} > {tol_o}"
     if dtype == torch.bfloat16:
         rel = eo / max(np.max(np.abs(ro)), 1e-30)
         assert rel <= REL_BF16, f"{what}: O relative {rel:.3e} > {REL_BF16}"
@@ -118,7 +128,7 @@ def test_stress_inputs(name, stress):
     q, k, v = workloads.attention_inputs(w, stress=stress, seed=3)
     o, lse = run_attn(q, k, v, w.scale)
     rows = None if name == "tiny" else np.arange(0, w.Sq, 7)
-    check(o, lse, q, k, v, w.scale, rows=rows, what=f"{name}/{stress}")
+    check(o, lse, q, k, v, w.scale, rows=rows, what=f"{name}/{stress}", out_rounding=True)
 
 
 RAGGED = [
