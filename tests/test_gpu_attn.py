@@ -201,7 +201,9 @@ def test_run_twice_is_bitwise_identical():
 
 
 def test_custom_scale():
+    # scale 0.37 at D=64 makes scores ~3x sharper than 1/sqrt(D): a stress-like
+    # case where |O| passes 2.56, so the stored-output rounding is added
     w = workloads.WORKLOADS["tiny"]
     q, k, v = workloads.attention_inputs(w, seed=9)
     o, lse = run_attn(q, k, v, 0.37)
-    check(o, lse, q, k, v, 0.37, what="scale 0.37")
+    check(o, lse, q, k, v, 0.37, what="scale 0.37", out_rounding=True)
