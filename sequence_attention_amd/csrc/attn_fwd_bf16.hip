@@ -8,14 +8,17 @@
 // ring hops consumes; LSE = ln sum_j exp(scale * q . k_j).
 //
 // Design (MI355X-first, not a translation of any CUDA kernel):
-//  * A workgroup of 4 waves owns 128 query rows of one (b, h); each wave owns
-//    32 rows and keeps its Q slice in registers for the whole key loop.
-//  * Keys are consumed in blocks of 64.  K and V blocks go from HBM/L2
-//    straight into LDS with global_load_lds_dwordx4 (no VGPR staging, no
-//    VALU), double-buffered so that the next block streams in while the
-//    current one is multiplied; one barrier per block.  Rows are stored with
-//    an XOR swizzle of their 16-byte chunks, chosen so that both operand
-//    reads below are bank-conflict free.
+//  * A workgroup of 8 waves (2 per SIMD) owns 256 query rows of one (b, h);
+//    each wave owns 32 rows and keeps its Q slice in registers for the whole
+//    key loop.  All 8 waves share each K/V block, so L2 traffic is one K/V
+//    pass per 256 query rows.
+//  * Keys are consumed in blocks of 64.  K and V blocks go from L2 straight
+//    into LDS with buffer_load_dwordx4 ... lds (no VGPR staging; the
+//    per-block address is a scalar buffer base, so no VALU either) through a
+//    4-stage ring: loads run three blocks ahead of the multiply, which hides
+//    L2 / HBM latency; one barrier per block.  Rows are stored with an XOR
+//    swizzle of their 16-byte chunks, chosen so that both operand reads
+//    below are bank-conflict free.
 //  * Both products use v_mfma_f32_32x32x16_bf16 in a transposed orientation:
 //    S^T = K Q^T and O^T = V^T P^T.  The S^T accumulator gives each lane one
 //    query and 16 keys, so the row max needs one swap with the partner lane
@@ -45,15 +48,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per block
 constexpr int kNumXcd = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9 family)
 
 struct Params {
   const uint16_t* q;
@@ -86,23 +89,36 @@ __device__ __forceinline__ int swz(int r) {
   else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
+// s_waitcnt with vmcnt(n), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 template <int D, bool kOutF32>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   constexpr int ROWB = D * 2;                 // bytes of one K/V row
   constexpr int BLKB = kBN * ROWB;            // bytes of one K or V block
   constexpr int NINSTR = BLKB / 1024;         // 1 KB direct loads per tensor per block
   constexpr int INSTR_W = NINSTR / kWaves;    // ... per wave
+  constexpr int LPB = 2 * INSTR_W;            // load instructions per block per wave (K + V)
   constexpr int KSTEPS = D / 16;              // MFMA k-steps over the head dim
   constexpr int DT = D / 32;                  // 32-row tiles of O^T
-  static_assert(NINSTR % kWaves == 0, "direct-load split");
+  static_assert(NINSTR % kWaves == 0 && INSTR_W >= 1, "direct-load split");
+  static_assert(2 * LPB < 16, "vmcnt budget");
 
-  // Two stages of K and V as four distinct LDS objects: the compiler can then
-  // prove that a direct load into one stage does not alias reads of the
-  // other and does not wait for the load before those reads.
-  __shared__ __attribute__((aligned(1024))) char k_st0[BLKB];
-  __shared__ __attribute__((aligned(1024))) char v_st0[BLKB];
-  __shared__ __attribute__((aligned(1024))) char k_st1[BLKB];
-  __shared__ __attribute__((aligned(1024))) char v_st1[BLKB];
+  // The ring's stages are distinct LDS objects: the compiler can then prove
+  // that a direct load into one stage does not alias reads of another and
+  // does not wait for the load before those reads.
+  __shared__ __attribute__((aligned(1024))) char k_s0[BLKB];
+  __shared__ __attribute__((aligned(1024))) char v_s0[BLKB];
+  __shared__ __attribute__((aligned(1024))) char k_s1[BLKB];
+  __shared__ __attribute__((aligned(1024))) char v_s1[BLKB];
+  __shared__ __attribute__((aligned(1024))) char k_s2[BLKB];
+  __shared__ __attribute__((aligned(1024))) char v_s2[BLKB];
+  __shared__ __attribute__((aligned(1024))) char k_s3[BLKB];
+  __shared__ __attribute__((aligned(1024))) char v_s3[BLKB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,25 +148,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     }
   }
 
-  // ---- direct global -> LDS loads of one K and one V block ----------------
+  // ---- direct L2 -> LDS loads of one K and one V block ---------------------
   // lane i of load instruction j fills LDS bytes j*1024 + 16*i of the block:
   // row = that offset / ROWB, physical chunk pc, logical chunk pc ^ swz(row).
+  // The block's base address is a scalar buffer descriptor, so the per-lane
+  // byte offset is loop-invariant; in the last, partial block rows past Skv
+  // are clamped to the last key (finite data; their scores are masked).
   int ld_row[INSTR_W], ld_col[INSTR_W];
+  uint32_t ld_off[INSTR_W];
 #pragma unroll
   for (int u = 0; u < INSTR_W; ++u) {
     const int off = (wave * INSTR_W + u) * 1024 + lane * 16;
     ld_row[u] = off / ROWB;
     ld_col[u] = (((off % ROWB) / 16) ^ swz<D>(ld_row[u])) * 8;  // element column
+    ld_off[u] = (uint32_t)(((size_t)ld_row[u] * rs + ld_col[u]) * 2);
   }
-  const int last_key = p.Skv - 1;
-  auto issue_block = [&](int j0, char* kdst, char* vdst) {
+  const int nblocks = (p.Skv + kBN - 1) / kBN;
+  auto issue = [&](int kb, char* kdst, char* vdst) {
+    const int j0 = kb * kBN;
+    const uint16_t* kb_ptr = kbase + (size_t)j0 * rs;
+    const uint16_t* vb_ptr = vbase + (size_t)j0 * rs;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb_ptr, (short)0, 0x7fffffff, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb_ptr, (short)0, 0x7fffffff, kBufferWord3);
+    const bool tail = j0 + kBN > p.Skv;
 #pragma unroll
     for (int u = 0; u < INSTR_W; ++u) {
-      const int j = min(j0 + ld_row[u], last_key);  // tail rows: any valid row, masked later
-      const size_t go = (size_t)j * rs + ld_col[u];
+      uint32_t off = ld_off[u];
+      if (tail) {
+        const int r = min(ld_row[u], p.Skv - 1 - j0);
+        off = (uint32_t)(((size_t)r * rs + ld_col[u]) * 2);
+      }
       const int dst = (wave * INSTR_W + u) * 1024;
-      __builtin_amdgcn_global_load_lds((gbl_void*)(kbase + go), (lds_void*)(kdst + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_void*)(vbase + go), (lds_void*)(vdst + dst), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + dst), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + dst), 16, off, 0, 0, 0);
     }
   };
 
@@ -173,20 +203,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   float lsum = 0.0f;         // this lane's share of the row sum
   const float c = p.scale * kLog2e;
 
-  const int nblocks = (p.Skv + kBN - 1) / kBN;
-  // one key block from stage ST; the next block is streamed into stage ST^1
+  // one key block from stage ST; block kb + 3 is streamed into stage ST - 1
   auto block = [&](auto stage, int kb) {
-    constexpr bool ST = decltype(stage)::value;
+    constexpr int ST = decltype(stage)::value;
     const int j0 = kb * kBN;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block kb landed
-    __syncthreads();                     // ... and everyone's; stage ST^1 is free again
-    if (kb + 1 < nblocks) {
-      if constexpr (ST) issue_block(j0 + kBN, k_st0, v_st0);
-      else issue_block(j0 + kBN, k_st1, v_st1);
+    // this wave's loads of block kb have landed once at most the loads of
+    // the (up to two) later blocks already issued are outstanding
+    const int ahead = min(2, nblocks - 1 - kb);
+    if (ahead == 2) wait_vmcnt<2 * LPB>();
+    else if (ahead == 1) wait_vmcnt<LPB>();
+    else wait_vmcnt<0>();
+    // Workgroup barrier without __syncthreads()'s release fence, which would
+    // wait for every outstanding load (vmcnt(0)) and drain the ring.  LDS
+    // reads of the stage being recycled completed before their MFMAs issued;
+    // the empty asm statements keep the compiler from moving memory accesses
+    // across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // everyone's loads of block kb landed; stage ST - 1 is free
+    asm volatile("" ::: "memory");
+    if (kb + 3 < nblocks) {
+      if constexpr (ST == 0) issue(kb + 3, k_s3, v_s3);
+      else if constexpr (ST == 1) issue(kb + 3, k_s0, v_s0);
+      else if constexpr (ST == 2) issue(kb + 3, k_s1, v_s1);
+      else issue(kb + 3, k_s2, v_s2);
     }
-    const char* ks = ST ? k_st1 : k_st0;
-    const char* vs = ST ? v_st1 : v_st0;
-
+    const char* ks = ST == 0 ? k_s0 : ST == 1 ? k_s1 : ST == 2 ? k_s2 : k_s3;
+    const char* vs = ST == 0 ? v_s0 : ST == 1 ? v_s1 : ST == 2 ? v_s2 : v_s3;
     // S^T = K Q^T: two 32-key tiles
     f32x16 s[2];
 #pragma unroll
@@ -262,10 +304,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         }
       }
   };
-  issue_block(0, k_st0, v_st0);
-  for (int kb = 0; kb < nblocks; kb += 2) {
-    block(std::integral_constant<bool, false>{}, kb);
-    if (kb + 1 < nblocks) block(std::integral_constant<bool, true>{}, kb + 1);
+  issue(0, k_s0, v_s0);
+  if (nblocks > 1) issue(1, k_s1, v_s1);
+  if (nblocks > 2) issue(2, k_s2, v_s2);
+  for (int kb = 0; kb < nblocks; kb += 4) {
+    block(std::integral_constant<int, 0>{}, kb);
+    if (kb + 1 < nblocks) block(std::integral_constant<int, 1>{}, kb + 1);
+    if (kb + 2 < nblocks) block(std::integral_constant<int, 2>{}, kb + 2);
+    if (kb + 3 < nblocks) block(std::integral_constant<int, 3>{}, kb + 3);
   }
 
   // ---- epilogue: normalise, store O (lane: one query, 16 dims per tile) ---
