@@ -22,7 +22,8 @@
 //  * Both products use v_mfma_f32_32x32x16_bf16 in a transposed orientation:
 //    S^T = K Q^T and O^T = V^T P^T.  The S^T accumulator gives each lane one
 //    query and 16 keys, so the row max needs one swap with the partner lane
-//    (l ^ 32), the row sum stays lane-local until the end, the rescale of
+//    (l ^ 32, v_permlane32_swap: a VALU op, no LDS round trip), the row sum
+//    stays lane-local until the end, the rescale of
 //    O^T is a per-lane scalar, and the accumulator registers, rounded to
 //    bf16, are directly the B operand of the PV MFMA.  The A operand V^T is
 //    read from row-major V with ds_read_b64_tr_b16 (gfx950 LDS transpose
@@ -257,7 +258,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const bool raise = (mx - m_used) * c > kRescaleLog2;
     if (__any(raise)) {
       const float m_new = raise ? mx : m_used;

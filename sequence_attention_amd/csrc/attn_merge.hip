@@ -14,13 +14,17 @@
 // writes one of each.  One thread owns 8 consecutive elements of a row
 // (16 bytes of bf16 / 32 bytes of fp32); the D/8 threads of a row read the
 // same two LSE values (one cache line serves many rows), and the row's
-// first thread writes the merged LSE.
+// first thread writes the merged LSE.  O moves with non-temporal loads and
+// stores (touched once).
 #include "dit_internal.h"
 
 namespace dit {
 namespace {
 
 constexpr int kThreads = 256;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -62,22 +66,22 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(void* __restrict__ o_ac
 
   float xa[8], xp[8], r[8];
   if constexpr (kF32) {
-    const float4* pa = reinterpret_cast<const float4*>(o_acc) + (size_t)idx * 2;
-    const float4* pp = reinterpret_cast<const float4*>(o_part) + (size_t)idx * 2;
-    const float4 a0 = pa[0], a1 = pa[1], p0 = pp[0], p1 = pp[1];
-    xa[0] = a0.x; xa[1] = a0.y; xa[2] = a0.z; xa[3] = a0.w;
-    xa[4] = a1.x; xa[5] = a1.y; xa[6] = a1.z; xa[7] = a1.w;
-    xp[0] = p0.x; xp[1] = p0.y; xp[2] = p0.z; xp[3] = p0.w;
-    xp[4] = p1.x; xp[5] = p1.y; xp[6] = p1.z; xp[7] = p1.w;
+    const f32x4* pa = reinterpret_cast<const f32x4*>(o_acc) + (size_t)idx * 2;
+    const f32x4* pp = reinterpret_cast<const f32x4*>(o_part) + (size_t)idx * 2;
+    const f32x4 a0 = __builtin_nontemporal_load(pa), a1 = __builtin_nontemporal_load(pa + 1);
+    const f32x4 p0 = __builtin_nontemporal_load(pp), p1 = __builtin_nontemporal_load(pp + 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xa[e] = a0[e]; xa[4 + e] = a1[e];
+      xp[e] = p0[e]; xp[4 + e] = p1[e];
+    }
   } else {
-    const uint4 a = reinterpret_cast<const uint4*>(o_acc)[idx];
-    const uint4 p = reinterpret_cast<const uint4*>(o_part)[idx];
-    const uint32_t wa4[4] = {a.x, a.y, a.z, a.w};
-    const uint32_t wp4[4] = {p.x, p.y, p.z, p.w};
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o_acc) + idx);
+    const u32x4 p = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o_part) + idx);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      xa[2 * w] = bf16_lo(wa4[w]); xa[2 * w + 1] = bf16_hi(wa4[w]);
-      xp[2 * w] = bf16_lo(wp4[w]); xp[2 * w + 1] = bf16_hi(wp4[w]);
+      xa[2 * w] = bf16_lo(a[w]); xa[2 * w + 1] = bf16_hi(a[w]);
+      xp[2 * w] = bf16_lo(p[w]); xp[2 * w + 1] = bf16_hi(p[w]);
     }
   }
 #pragma unroll
@@ -87,16 +91,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(void* __restrict__ o_ac
     r[e] = ta + tp;
   }
   if constexpr (kF32) {
-    float4* pa = reinterpret_cast<float4*>(o_acc) + (size_t)idx * 2;
-    pa[0] = make_float4(r[0], r[1], r[2], r[3]);
-    pa[1] = make_float4(r[4], r[5], r[6], r[7]);
+    f32x4* pa = reinterpret_cast<f32x4*>(o_acc) + (size_t)idx * 2;
+    __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]}, pa);
+    __builtin_nontemporal_store(f32x4{r[4], r[5], r[6], r[7]}, pa + 1);
   } else {
-    uint4 out;
-    out.x = f32_to_bf16_rne(r[0]) | (f32_to_bf16_rne(r[1]) << 16);
-    out.y = f32_to_bf16_rne(r[2]) | (f32_to_bf16_rne(r[3]) << 16);
-    out.z = f32_to_bf16_rne(r[4]) | (f32_to_bf16_rne(r[5]) << 16);
-    out.w = f32_to_bf16_rne(r[6]) | (f32_to_bf16_rne(r[7]) << 16);
-    reinterpret_cast<uint4*>(o_acc)[idx] = out;
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) out[w] = f32_to_bf16_rne(r[2 * w]) | (f32_to_bf16_rne(r[2 * w + 1]) << 16);
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(o_acc) + idx);
   }
   if (chunk == 0) lse_acc[lse_idx] = empty ? -INFINITY : m + __logf(wsum);
 }

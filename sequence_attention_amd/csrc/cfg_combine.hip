@@ -5,8 +5,8 @@
 // p_uncond + g * (p_cond - p_uncond).  Evaluated per element as one fused
 // multiply-add fmaf(g, p_cond - p_uncond, p_uncond) in fp32.
 //
-// HBM-bound elementwise pass: 16-byte vector loads of both inputs, one
-// 16-byte store, several vectors per thread in flight.  `out` may alias an
+// HBM-bound elementwise pass: 16-byte non-temporal vector loads of both
+// inputs and one 16-byte non-temporal store per thread.  `out` may alias an
 // input exactly (each element is read before it is written by the same
 // thread), so no restrict qualifiers.
 #include "dit_internal.h"
@@ -15,31 +15,32 @@ namespace dit {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;
+constexpr int kVecPerThread = 1;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void cfg_f32_kernel(const float* u, const float* c, float* out,
                                                            int64_t n, float g) {
   const int64_t nvec = n >> 2;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * kVecPerThread) + threadIdx.x;
-  float4 uu[kVecPerThread], cc[kVecPerThread];
+  f32x4 uu[kVecPerThread], cc[kVecPerThread];
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
     const int64_t v = base + (int64_t)i * kThreads;
     if (v < nvec) {
-      uu[i] = reinterpret_cast<const float4*>(u)[v];
-      cc[i] = reinterpret_cast<const float4*>(c)[v];
+      uu[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(u) + v);
+      cc[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c) + v);
     }
   }
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
     const int64_t v = base + (int64_t)i * kThreads;
     if (v < nvec) {
-      float4 r;
-      r.x = __builtin_fmaf(g, cc[i].x - uu[i].x, uu[i].x);
-      r.y = __builtin_fmaf(g, cc[i].y - uu[i].y, uu[i].y);
-      r.z = __builtin_fmaf(g, cc[i].z - uu[i].z, uu[i].z);
-      r.w = __builtin_fmaf(g, cc[i].w - uu[i].w, uu[i].w);
-      reinterpret_cast<float4*>(out)[v] = r;
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(g, cc[i][e] - uu[i][e], uu[i][e]);
+      __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(out) + v);
     }
   }
   // scalar tail (n % 4 elements), taken by the first threads of block 0
@@ -64,32 +65,29 @@ __global__ __launch_bounds__(kThreads) void cfg_bf16_kernel(const uint16_t* u, c
                                                             uint16_t* out, int64_t n, float g) {
   const int64_t nvec = n >> 3;  // 8 bf16 per 16-byte vector
   const int64_t base = (int64_t)blockIdx.x * (kThreads * kVecPerThread) + threadIdx.x;
-  uint4 uu[kVecPerThread], cc[kVecPerThread];
+  u32x4 uu[kVecPerThread], cc[kVecPerThread];
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
     const int64_t v = base + (int64_t)i * kThreads;
     if (v < nvec) {
-      uu[i] = reinterpret_cast<const uint4*>(u)[v];
-      cc[i] = reinterpret_cast<const uint4*>(c)[v];
+      uu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(u) + v);
+      cc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c) + v);
     }
   }
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
     const int64_t v = base + (int64_t)i * kThreads;
     if (v < nvec) {
-      const uint32_t* pu = &uu[i].x;
-      const uint32_t* pc = &cc[i].x;
-      uint4 r;
-      uint32_t* pr = &r.x;
+      u32x4 r;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float u0 = bf16_to_f32(pu[w] & 0xffffu), u1 = bf16_to_f32(pu[w] >> 16);
-        const float c0 = bf16_to_f32(pc[w] & 0xffffu), c1 = bf16_to_f32(pc[w] >> 16);
+        const float u0 = bf16_to_f32(uu[i][w] & 0xffffu), u1 = bf16_to_f32(uu[i][w] >> 16);
+        const float c0 = bf16_to_f32(cc[i][w] & 0xffffu), c1 = bf16_to_f32(cc[i][w] >> 16);
         const uint32_t r0 = f32_to_bf16_rne(__builtin_fmaf(g, c0 - u0, u0));
         const uint32_t r1 = f32_to_bf16_rne(__builtin_fmaf(g, c1 - u1, u1));
-        pr[w] = r0 | (r1 << 16);
+        r[w] = r0 | (r1 << 16);
       }
-      reinterpret_cast<uint4*>(out)[v] = r;
+      __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(out) + v);
     }
   }
   if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {

@@ -250,6 +250,9 @@ dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   // tile counts are 32-bit; the fp32 path puts H and B on grid y / z
   if ((int64_t)B * H * ((Sq + 127) / 128) >= (int64_t)1 << 31)
     return fail(DIT_ERR_UNSUPPORTED, "too many query tiles");
+  // the bf16 kernel addresses a 64-row K/V block with 32-bit byte offsets
+  if ((int64_t)H * D * 2 * 64 >= ((int64_t)1 << 30))
+    return fail(DIT_ERR_UNSUPPORTED, "row stride H*D=%lld too large", (long long)H * D);
   if (in_dtype == DIT_F32 && (H > 65535 || B > 65535))
     return fail(DIT_ERR_UNSUPPORTED, "fp32 path limits B and H to 65535");
 
