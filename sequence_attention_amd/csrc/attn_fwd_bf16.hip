@@ -38,6 +38,7 @@
 //  * Work tiles are renumbered so that consecutive query tiles of one head
 //    land on the same XCD (workgroups are dealt round-robin over the 8
 //    XCDs): the head's K/V stream is then served from that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "dit_internal.h"
@@ -48,6 +49,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 8;
@@ -58,6 +62,8 @@ constexpr int kNumXcd = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9 family)
+constexpr uint64_t kMaxSplit = 8;        // key chunks per tile in the split round
+constexpr int kScopeAgent = 16;           // buffer cache policy: sc1, device-scope coherent
 
 struct Params {
   const uint16_t* q;
@@ -65,13 +71,20 @@ struct Params {
   const uint16_t* v;
   void* o;
   float* lse;
+  float* part;    // partial-result slots, one per workgroup of the split round
+  int32_t* cnt;   // arrival counters of the split tiles, zero between launches
   int32_t Sq, Skv, H;
   int32_t n_qtiles;
-  uint32_t n_tiles;
+  int32_t nblocks;   // key blocks per tile
+  uint32_t n_whole;  // tiles taken whole, one per workgroup
+  uint32_t split;    // pieces per tile of the split round (>= 2 when used)
+  uint32_t split_wgs;  // workgroups of the split round: split x (tiles - n_whole)
   float scale;
 };
 
-__device__ __forceinline__ uint32_t tile_of_block(uint32_t bid, uint32_t n) {
+// Workgroups are dealt round-robin over the XCDs; renumber them so that each
+// XCD owns one contiguous range of logical indices (a bijection on [0, n)).
+__device__ __forceinline__ uint32_t logical_wg(uint32_t bid, uint32_t n) {
   const uint32_t xcd = bid % kNumXcd, local = bid / kNumXcd;
   const uint32_t q = n / kNumXcd, r = n % kNumXcd;
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
@@ -97,6 +110,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// Floats of one partial-result slot: per lane the D/2 accumulator registers
+// of O^T, then the running max and the lane's share of the row sum.
+template <int D>
+constexpr size_t slot_floats() {
+  return (size_t)kWaves * 64 * (D / 2 + 2);
+}
+
 template <int D, bool kOutF32>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   constexpr int ROWB = D * 2;                 // bytes of one K/V row
@@ -106,6 +126,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   constexpr int LPB = 2 * INSTR_W;            // load instructions per block per wave (K + V)
   constexpr int KSTEPS = D / 16;              // MFMA k-steps over the head dim
   constexpr int DT = D / 32;                  // 32-row tiles of O^T
+  constexpr size_t SLOT = slot_floats<D>();
+  constexpr size_t ML_OFF = (size_t)kWaves * 64 * (D / 2);
   static_assert(NINSTR % kWaves == 0 && INSTR_W >= 1, "direct-load split");
   static_assert(2 * LPB < 16, "vmcnt budget");
 
@@ -120,36 +142,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char v_s2[BLKB];
   __shared__ __attribute__((aligned(1024))) char k_s3[BLKB];
   __shared__ __attribute__((aligned(1024))) char v_s3[BLKB];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int g = lane >> 5;
-
-  const uint32_t tile = tile_of_block(blockIdx.x, p.n_tiles);
-  const int qt = tile % p.n_qtiles;
-  const int bh = tile / p.n_qtiles;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
   const size_t rs = (size_t)p.H * D;  // elements between sequence rows
-  const uint16_t* kbase = p.k + (size_t)b * p.Skv * rs + (size_t)h * D;
-  const uint16_t* vbase = p.v + (size_t)b * p.Skv * rs + (size_t)h * D;
+  const int nblocks = p.nblocks;
+  const float c = p.scale * kLog2e;
 
-  // ---- Q slice of this wave in registers: B operand of S^T = K Q^T -------
-  const int q_row = qt * kBM + wave * 32 + l32;
-  const bool q_ok = q_row < p.Sq;
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t* qp = p.q + ((size_t)b * p.Sq + (q_ok ? q_row : 0)) * rs + (size_t)h * D + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const uint4 u = q_ok ? *reinterpret_cast<const uint4*>(qp + kk * 16) : make_uint4(0, 0, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-
-  // ---- direct L2 -> LDS loads of one K and one V block ---------------------
+  // ---- direct L2 -> LDS load geometry ----------------------------------------
   // lane i of load instruction j fills LDS bytes j*1024 + 16*i of the block:
   // row = that offset / ROWB, physical chunk pc, logical chunk pc ^ swz(row).
   // The block's base address is a scalar buffer descriptor, so the per-lane
@@ -164,26 +168,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     ld_col[u] = (((off % ROWB) / 16) ^ swz<D>(ld_row[u])) * 8;  // element column
     ld_off[u] = (uint32_t)(((size_t)ld_row[u] * rs + ld_col[u]) * 2);
   }
-  const int nblocks = (p.Skv + kBN - 1) / kBN;
-  auto issue = [&](int kb, char* kdst, char* vdst) {
-    const int j0 = kb * kBN;
-    const uint16_t* kb_ptr = kbase + (size_t)j0 * rs;
-    const uint16_t* vb_ptr = vbase + (size_t)j0 * rs;
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb_ptr, (short)0, 0x7fffffff, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb_ptr, (short)0, 0x7fffffff, kBufferWord3);
-    const bool tail = j0 + kBN > p.Skv;
-#pragma unroll
-    for (int u = 0; u < INSTR_W; ++u) {
-      uint32_t off = ld_off[u];
-      if (tail) {
-        const int r = min(ld_row[u], p.Skv - 1 - j0);
-        off = (uint32_t)(((size_t)r * rs + ld_col[u]) * 2);
-      }
-      const int dst = (wave * INSTR_W + u) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + dst), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + dst), 16, off, 0, 0, 0);
-    }
-  };
 
   // ---- per-lane LDS read offsets ------------------------------------------
   // K operand (ds_read_b128): row 32t + l32, logical chunk 2kk + g.
@@ -195,152 +179,283 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   const int v_rsub = i16 >> 2;         // key row inside the 4-row group
   const int v_piece = i16 & 3;         // 4-dim piece inside the 16 dims
 
-  f32x16 oacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
-  float m_used = -INFINITY;  // running reference max of raw scores q . k
-  float lsum = 0.0f;         // this lane's share of the row sum
-  const float c = p.scale * kLog2e;
+  // The workgroup's segment: key blocks [kb0, kb1) of one tile.  The first
+  // n_whole workgroups take one tile each; the rest take key chunk
+  // (j % split) of tile n_whole + j / split.  Workgroups are dealt
+  // round-robin over the XCDs in index order; both ranges are renumbered so
+  // that each XCD gets contiguous tiles (one head's K/V then streams through
+  // that XCD's L2) and an even share of both kinds (n_whole is a multiple of
+  // the XCD count whenever chunks follow).
+  {
+    const bool whole = blockIdx.x < p.n_whole;
+    const uint32_t j = whole ? logical_wg(blockIdx.x, p.n_whole) : logical_wg(blockIdx.x - p.n_whole, p.split_wgs);
+    const uint32_t piece = whole ? 0 : j % p.split;
+    const uint32_t tile = whole ? j : p.n_whole + j / p.split;
+    const int kb0 = whole ? 0 : (int)((uint64_t)piece * nblocks / p.split);
+    const int kb1 = whole ? nblocks : (int)((uint64_t)(piece + 1) * nblocks / p.split);
 
-  // one key block from stage ST; block kb + 3 is streamed into stage ST - 1
-  auto block = [&](auto stage, int kb) {
-    constexpr int ST = decltype(stage)::value;
-    const int j0 = kb * kBN;
-    // this wave's loads of block kb have landed once at most the loads of
-    // the (up to two) later blocks already issued are outstanding
-    const int ahead = min(2, nblocks - 1 - kb);
-    if (ahead == 2) wait_vmcnt<2 * LPB>();
-    else if (ahead == 1) wait_vmcnt<LPB>();
-    else wait_vmcnt<0>();
-    // Workgroup barrier without __syncthreads()'s release fence, which would
-    // wait for every outstanding load (vmcnt(0)) and drain the ring.  LDS
-    // reads of the stage being recycled completed before their MFMAs issued;
-    // the empty asm statements keep the compiler from moving memory accesses
-    // across the barrier.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // everyone's loads of block kb landed; stage ST - 1 is free
-    asm volatile("" ::: "memory");
-    if (kb + 3 < nblocks) {
-      if constexpr (ST == 0) issue(kb + 3, k_s3, v_s3);
-      else if constexpr (ST == 1) issue(kb + 3, k_s0, v_s0);
-      else if constexpr (ST == 2) issue(kb + 3, k_s1, v_s1);
-      else issue(kb + 3, k_s2, v_s2);
-    }
-    const char* ks = ST == 0 ? k_s0 : ST == 1 ? k_s1 : ST == 2 ? k_s2 : k_s3;
-    const char* vs = ST == 0 ? v_s0 : ST == 1 ? v_s1 : ST == 2 ? v_s2 : v_s3;
-    // S^T = K Q^T: two 32-key tiles
-    f32x16 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-      const char* krow = ks + (32 * t + l32) * ROWB;
+    const int qt = tile % p.n_qtiles;
+    const int bh = tile / p.n_qtiles;
+    const int h = bh % p.H;
+    const int b = bh / p.H;
+    const uint16_t* kbase = p.k + (size_t)b * p.Skv * rs + (size_t)h * D;
+    const uint16_t* vbase = p.v + (size_t)b * p.Skv * rs + (size_t)h * D;
+
+    // ---- Q slice of this wave in registers: B operand of S^T = K Q^T -----
+    const int q_row = qt * kBM + wave * 32 + l32;
+    const bool q_ok = q_row < p.Sq;
+    bf16x8 qf[KSTEPS];
+    {
+      const uint16_t* qp = p.q + ((size_t)b * p.Sq + (q_ok ? q_row : 0)) * rs + (size_t)h * D + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        const uint4 a = *reinterpret_cast<const uint4*>(krow + (((2 * kk + g) ^ k_sw) << 4));
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], s[t], 0, 0, 0);
+        const uint4 u = q_ok ? *reinterpret_cast<const uint4*>(qp + kk * 16) : make_uint4(0, 0, 0, 0);
+        qf[kk] = __builtin_bit_cast(bf16x8, u);
       }
     }
-    // lane holds S^T[key = 32t + 8(r/4) + 4g + r%4][query l32]
-    if (j0 + kBN > p.Skv) {
+
+    auto issue = [&](int kb, char* kdst, char* vdst) __attribute__((always_inline)) {
+      const int j0 = kb * kBN;
+      const uint16_t* kb_ptr = kbase + (size_t)j0 * rs;
+      const uint16_t* vb_ptr = vbase + (size_t)j0 * rs;
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb_ptr, (short)0, 0x7fffffff, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb_ptr, (short)0, 0x7fffffff, kBufferWord3);
+      const bool tail = j0 + kBN > p.Skv;
+#pragma unroll
+      for (int u = 0; u < INSTR_W; ++u) {
+        uint32_t off = ld_off[u];
+        if (tail) {
+          const int r = min(ld_row[u], p.Skv - 1 - j0);
+          off = (uint32_t)(((size_t)r * rs + ld_col[u]) * 2);
+        }
+        const int dst = (wave * INSTR_W + u) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + dst), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + dst), 16, off, 0, 0, 0);
+      }
+    };
+
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+    float m_used = -INFINITY;  // running reference max of raw scores q . k
+    float lsum = 0.0f;         // this lane's share of the row sum
+
+    // one key block from stage ST; block kb + 3 is streamed into stage ST - 1
+    auto block = [&](auto stage, int kb) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage)::value;
+      const int j0 = kb * kBN;
+      // this wave's loads of block kb have landed once at most the loads of
+      // the (up to two) later blocks already issued are outstanding
+      const int ahead = min(2, kb1 - 1 - kb);
+      if (ahead == 2) wait_vmcnt<2 * LPB>();
+      else if (ahead == 1) wait_vmcnt<LPB>();
+      else wait_vmcnt<0>();
+      // Workgroup barrier without __syncthreads()'s release fence, which
+      // would wait for every outstanding load (vmcnt(0)) and drain the ring.
+      // LDS reads of the stage being recycled completed before their MFMAs
+      // issued; the empty asm statements keep the compiler from moving
+      // memory accesses across the barrier.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();  // everyone's loads of block kb landed; stage ST - 1 is free
+      asm volatile("" ::: "memory");
+      if (kb + 3 < kb1) {
+        if constexpr (ST == 0) issue(kb + 3, k_s3, v_s3);
+        else if constexpr (ST == 1) issue(kb + 3, k_s0, v_s0);
+        else if constexpr (ST == 2) issue(kb + 3, k_s1, v_s1);
+        else issue(kb + 3, k_s2, v_s2);
+      }
+      const char* ks = ST == 0 ? k_s0 : ST == 1 ? k_s1 : ST == 2 ? k_s2 : k_s3;
+      const char* vs = ST == 0 ? v_s0 : ST == 1 ? v_s1 : ST == 2 ? v_s2 : v_s3;
+      // S^T = K Q^T: two 32-key tiles
+      f32x16 s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+        const char* krow = ks + (32 * t + l32) * ROWB;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const uint4 a = *reinterpret_cast<const uint4*>(krow + (((2 * kk + g) ^ k_sw) << 4));
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], s[t], 0, 0, 0);
+        }
+      }
+      // lane holds S^T[key = 32t + 8(r/4) + 4g + r%4][query l32]
+      if (j0 + kBN > p.Skv) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= p.Skv) s[t][r] = -INFINITY;
+          }
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const bool raise = (mx - m_used) * c > kRescaleLog2;
+      if (__any(raise)) {
+        const float m_new = raise ? mx : m_used;
+        const float alpha = __builtin_amdgcn_exp2f((m_used - m_new) * c);
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        m_used = m_new;
+      }
+      const float mc = m_used * c;
+
+      // LSE needs the row sum of the unrounded P: a bf16-rounded sum would be
+      // off by up to 2^-9 relative (about 2e-3 in LSE) on near one-hot rows.
+      bf16x8 pb[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= p.Skv) s[t][r] = -INFINITY;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -mc));
+          lsum += pr;
+          pb[t][r >> 3][r & 7] = (__bf16)pr;
         }
-    }
-    float mx = s[0][0];
+
+      // O^T += V^T P^T: 4 key steps of 16 keys
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        for (int jh = 0; jh < 2; ++jh) {
+          const int kbase16 = (2 * t + jh) * 16;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            i16x4 half[2];
+#pragma unroll
+            for (int rd = 0; rd < 2; ++rd) {
+              const int row = kbase16 + 8 * rd + 4 * g + v_rsub;
+              const int d = dt * 32 + 16 * g16 + 4 * v_piece;
+              const int off = row * ROWB + ((((d >> 3) ^ swz<D>(row))) << 4) + ((d & 4) << 1);
+              half[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vs + off));
+            }
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t][jh], oacc[dt], 0, 0, 0);
+          }
+        }
+    };
+    issue(kb0, k_s0, v_s0);
+    if (kb0 + 1 < kb1) issue(kb0 + 1, k_s1, v_s1);
+    if (kb0 + 2 < kb1) issue(kb0 + 2, k_s2, v_s2);
+    for (int kb = kb0; kb < kb1; kb += 4) {
+      block(std::integral_constant<int, 0>{}, kb);
+      if (kb + 1 < kb1) block(std::integral_constant<int, 1>{}, kb + 1);
+      if (kb + 2 < kb1) block(std::integral_constant<int, 2>{}, kb + 2);
+      if (kb + 3 < kb1) block(std::integral_constant<int, 3>{}, kb + 3);
     }
-    const bool raise = (mx - m_used) * c > kRescaleLog2;
-    if (__any(raise)) {
-      const float m_new = raise ? mx : m_used;
-      const float alpha = __builtin_amdgcn_exp2f((m_used - m_new) * c);
-      lsum *= alpha;
+
+    // ---- normalise and store O and LSE (lane: one query, 16 dims per tile) --
+    auto store_out = [&](const f32x16 (&acc)[DT], float m_ref, float l_lane) __attribute__((always_inline)) {
+      const float ltot = l_lane + __shfl_xor(l_lane, 32);
+      if (!q_ok) return;
+      const float inv = 1.0f / ltot;
+      const size_t orow = ((size_t)b * p.Sq + q_row) * rs + (size_t)h * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      m_used = m_new;
-    }
-    const float mc = m_used * c;
-
-    // LSE needs the row sum of the unrounded P: a bf16-rounded sum would be
-    // off by up to 2^-9 relative (about 2e-3 in LSE) on near one-hot rows.
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -mc));
-        lsum += pr;
-        pb[t][r >> 3][r & 7] = (__bf16)pr;
-      }
-
-    // O^T += V^T P^T: 4 key steps of 16 keys
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int jh = 0; jh < 2; ++jh) {
-        const int kbase16 = (2 * t + jh) * 16;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          i16x4 half[2];
-#pragma unroll
-          for (int rd = 0; rd < 2; ++rd) {
-            const int row = kbase16 + 8 * rd + 4 * g + v_rsub;
-            const int d = dt * 32 + 16 * g16 + 4 * v_piece;
-            const int off = row * ROWB + ((((d >> 3) ^ swz<D>(row))) << 4) + ((d & 4) << 1);
-            half[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vs + off));
+        for (int u = 0; u < 4; ++u) {
+          const int d = dt * 32 + 8 * u + 4 * g;
+          const float o0 = acc[dt][4 * u + 0] * inv, o1 = acc[dt][4 * u + 1] * inv;
+          const float o2 = acc[dt][4 * u + 2] * inv, o3 = acc[dt][4 * u + 3] * inv;
+          if constexpr (kOutF32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.o) + orow + d) = make_float4(o0, o1, o2, o3);
+          } else {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 w;
+            w[0] = (__bf16)o0; w[1] = (__bf16)o1; w[2] = (__bf16)o2; w[3] = (__bf16)o3;
+            *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + orow + d) = w;
           }
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t][jh], oacc[dt], 0, 0, 0);
         }
-      }
-  };
-  issue(0, k_s0, v_s0);
-  if (nblocks > 1) issue(1, k_s1, v_s1);
-  if (nblocks > 2) issue(2, k_s2, v_s2);
-  for (int kb = 0; kb < nblocks; kb += 4) {
-    block(std::integral_constant<int, 0>{}, kb);
-    if (kb + 1 < nblocks) block(std::integral_constant<int, 1>{}, kb + 1);
-    if (kb + 2 < nblocks) block(std::integral_constant<int, 2>{}, kb + 2);
-    if (kb + 3 < nblocks) block(std::integral_constant<int, 3>{}, kb + 3);
-  }
+      if (p.lse != nullptr && g == 0)
+        p.lse[((size_t)b * p.H + h) * p.Sq + q_row] = m_ref * p.scale + __logf(ltot);
+    };
 
-  // ---- epilogue: normalise, store O (lane: one query, 16 dims per tile) ---
-  const float ltot = lsum + __shfl_xor(lsum, 32);
-  if (!q_ok) return;
-  const float inv = 1.0f / ltot;
-  const size_t orow = ((size_t)b * p.Sq + q_row) * rs + (size_t)h * D;
+    if (whole) {
+      store_out(oacc, m_used, lsum);
+    } else {
+      // ---- split tile: publish this piece, the last piece to arrive merges --
+      // The tile's pieces are the workgroups first .. first + split - 1 of
+      // the split round, in key order; each owns the slot of its index.
+      const uint32_t first = j - piece;
+      auto slot_of = [&](uint32_t w) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc(p.part + (size_t)w * SLOT, (short)0,
+                                                 (int)(SLOT * sizeof(float)), kBufferWord3);
+      };
+      // byte offsets inside a slot: lane-contiguous 16-byte pieces of O^T,
+      // then (running max, row-sum share) per lane
+      auto o_off = [&](int dt, int u) __attribute__((always_inline)) {
+        return (int)((((dt * 4 + u) * kWaves + wave) * 64 + lane) * 16);
+      };
+      const int ml_off = (int)(ML_OFF * sizeof(float)) + (wave * 64 + lane) * 8;
+      {
+        const __amdgpu_buffer_rsrc_t sl = slot_of(j);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = dt * 32 + 8 * u + 4 * g;
-      const float o0 = oacc[dt][4 * u + 0] * inv, o1 = oacc[dt][4 * u + 1] * inv;
-      const float o2 = oacc[dt][4 * u + 2] * inv, o3 = oacc[dt][4 * u + 3] * inv;
-      if constexpr (kOutF32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(p.o) + orow + d) = make_float4(o0, o1, o2, o3);
-      } else {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 w;
-        w[0] = (__bf16)o0; w[1] = (__bf16)o1; w[2] = (__bf16)o2; w[3] = (__bf16)o3;
-        *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + orow + d) = w;
+          for (int u = 0; u < 4; ++u) {
+            const f32x4 v4 = {oacc[dt][4 * u], oacc[dt][4 * u + 1], oacc[dt][4 * u + 2], oacc[dt][4 * u + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), sl, o_off(dt, u), 0, kScopeAgent);
+          }
+        const u32x2 ml = {__float_as_uint(m_used), __float_as_uint(lsum)};
+        __builtin_amdgcn_raw_buffer_store_b64(ml, sl, ml_off, 0, kScopeAgent);
+      }
+      // Slot traffic uses device-scope coherent accesses (they bypass the
+      // XCD-private L2 state), so completion of this wave's stores is all the
+      // release the counter increment needs; no cache-wide writeback or
+      // invalidate that would also evict the other workgroups' K/V lines.
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      int32_t* counter = p.cnt + (tile - p.n_whole);
+      if (tid == 0) s_last = atomicAdd(counter, 1) == (int)p.split - 1;
+      __syncthreads();
+      if (s_last) {
+        // merge all pieces in key order, this one re-read from its slot too,
+        // so the result does not depend on which piece arrived last
+        float M = -INFINITY;
+        for (uint32_t w = first; w < first + p.split; ++w) {
+          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(slot_of(w), ml_off, 0, kScopeAgent);
+          M = fmaxf(M, __uint_as_float(ml[0]));
+        }
+        f32x16 acc[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
+        float l = 0.0f;
+        for (uint32_t w = first; w < first + p.split; ++w) {
+          const __amdgpu_buffer_rsrc_t sl = slot_of(w);
+          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(sl, ml_off, 0, kScopeAgent);
+          const float alpha = __builtin_amdgcn_exp2f((__uint_as_float(ml[0]) - M) * c);
+          l += alpha * __uint_as_float(ml[1]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const f32x4 v4 = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(sl, o_off(dt, u), 0, kScopeAgent));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[dt][4 * u + e] += alpha * v4[e];
+            }
+        }
+        store_out(acc, M, l);
+        if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  if (p.lse != nullptr && g == 0)
-    p.lse[((size_t)b * p.H + h) * p.Sq + q_row] = m_used * p.scale + __logf(ltot);
+  }
 }
 
 template <int D, bool kOutF32>
@@ -355,9 +470,45 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.Skv = a.Skv;
   p.H = a.H;
   p.n_qtiles = (a.Sq + kBM - 1) / kBM;
-  p.n_tiles = (uint32_t)p.n_qtiles * a.H * a.B;
+  const uint64_t n_tiles = (uint64_t)p.n_qtiles * a.H * a.B;
+  p.nblocks = (a.Skv + kBN - 1) / kBN;
   p.scale = a.scale;
-  attn_bf16_kernel<D, kOutF32><<<p.n_tiles, kThreads, 0, stream>>>(p);
+  if (n_tiles == 0 || p.nblocks == 0) return hipSuccess;
+
+  // One workgroup per tile, in rounds of `slots` resident workgroups.  When
+  // the last round would leave many of them idle, its tiles are instead cut
+  // into `split` key chunks, one workgroup each, merged by the online-softmax
+  // rule.
+  static int occupancy[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (occupancy[dev] == 0) {
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, kOutF32>, kThreads, 0);
+    if (e != hipSuccess) return e;
+    occupancy[dev] = per_cu > 0 ? per_cu : 1;
+  }
+  int cus = 0;
+  if ((e = device_cu_count(&cus)) != hipSuccess) return e;
+  const uint64_t slots = (uint64_t)cus * occupancy[dev];
+  const uint64_t last = n_tiles % slots;  // tiles of the last, partial round
+  uint64_t split = last == 0 ? 1 : std::min<uint64_t>({kMaxSplit, slots / last, (uint64_t)p.nblocks});
+  if (split < 2) split = 1;
+  p.n_whole = (uint32_t)(split > 1 ? n_tiles - last : n_tiles);
+  p.split = (uint32_t)split;
+  p.split_wgs = (uint32_t)(split > 1 ? last * split : 0);
+  const uint64_t grid = (uint64_t)p.n_whole + p.split_wgs;
+
+  void* cnt = nullptr;
+  void* part = nullptr;
+  e = stream_workspace(stream, std::max<uint64_t>(last, 1) * sizeof(int32_t),
+                       std::max<uint64_t>(p.split_wgs, 1) * slot_floats<D>() * sizeof(float), &cnt, &part);
+  if (e != hipSuccess) return e;
+  p.cnt = static_cast<int32_t*>(cnt);
+  p.part = static_cast<float*>(part);
+  attn_bf16_kernel<D, kOutF32><<<(unsigned)grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 

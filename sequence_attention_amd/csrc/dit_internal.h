@@ -31,6 +31,21 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   return (__umulhi(n, f.m) + n) >> f.s;
 }
 
+// ---- device resources ---------------------------------------------------------
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device (queried once per device).
+hipError_t device_cu_count(int* cus);
+
+// Device memory private to (current device, stream), allocated on first use
+// and grown on demand, kept until the process ends: `zeroed_bytes` of
+// memory that is all-zero when handed out (a fresh allocation is zero-filled
+// on `stream`; kernels that use it must leave it zero again) and
+// `scratch_bytes` of scratch with undefined contents.  Growth first waits for
+// the stream's earlier work, which may still use the old allocation.
+hipError_t stream_workspace(hipStream_t stream, size_t zeroed_bytes, size_t scratch_bytes,
+                            void** zeroed, void** scratch);
+
 // ---- Ulysses permutes -------------------------------------------------------
 enum PermuteKind : int {
   PACK_SEQ_TO_HEAD = 0,

@@ -207,3 +207,40 @@ def test_custom_scale():
     q, k, v = workloads.attention_inputs(w, seed=9)
     o, lse = run_attn(q, k, v, 0.37)
     check(o, lse, q, k, v, 0.37, what="scale 0.37", out_rounding=True)
+
+
+# Shapes whose last round of tiles is cut into key chunks merged by the
+# last-arriving chunk (on a 256-CU device: 8, 8, 3 and 4 chunks per tile;
+# the fourth mixes tiles taken whole with split ones), run back to back so
+# that the per-stream workspace is reused across different tile counts.
+SPLIT_SEQUENCE = [
+    # B, Sq, Skv, H, D
+    (1, 1000, 1000, 8, 128),   # 32 tiles, all split
+    (1, 300, 5000, 2, 128),    # 4 tiles of 79 key blocks
+    (2, 3000, 2500, 3, 64),    # 72 tiles
+    (1, 4000, 700, 20, 64),    # 320 tiles: 256 whole, 64 split; ragged rows and keys
+    (1, 1000, 1000, 8, 128),   # back to the first shape
+]
+
+
+def test_split_tiles_and_workspace_reuse():
+    for i, shape in enumerate(SPLIT_SEQUENCE):
+        B, Sq, Skv, H, D = shape
+        log(f"attn bf16 split-tile sequence {i} {shape}")
+        w = workloads.Workload("split", B=B, Sq=Sq, Skv=Skv, H=H, D=D, R=1, S=Skv, H_total=H, U=1)
+        q, k, v = workloads.attention_inputs(w, seed=100 + i)
+        o, lse = run_attn(q, k, v, w.scale)
+        check(o, lse, q, k, v, w.scale, what=f"split {shape}")
+
+
+def test_side_stream_matches_default_stream():
+    w = workloads.WORKLOADS["flux"]
+    log("attn bf16 flux on a second stream")
+    q, k, v = (t.to(DEV) for t in workloads.attention_inputs(w, seed=5))
+    o1, l1 = sa.dit_attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = sa.dit_attn_fwd(q, k, v)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
