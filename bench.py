@@ -17,12 +17,14 @@ Ulysses degree 2, ring degree 1):
   F   CFG combine                 [2,4096,64] fp32 latent prediction, g = 4
 
 `value` is the step's algorithmic attention FLOP (4*B*H*Sq*Skv*D) divided by
-the measured step time.  Inputs are resident in HBM before timing; input
-sets rotate so that successive steps do not find their data in the 256 MB
-Infinity Cache.  The JSON line also carries the attention kernel's roofline
-(HIP events on the launch stream), per-kernel times, side measurements of
-the headline permute (Wan [1,9450,40,128]) and of the ring merge, and the
-fp64 CPU oracle timed on this host on the same workload.
+the measured step time (K steps bracketed by two HIP events on the launch
+stream).  Inputs are resident in HBM before timing; input sets rotate so
+that successive steps do not find their data in the 256 MB Infinity Cache.
+The JSON line also carries the attention kernel's roofline (its average
+launch duration: K back-to-back launches bracketed by events), per-kernel
+times, attention at every DiT shard shape, side measurements of the headline
+permute (Wan [1,9450,40,128]) and of the ring merge, and the fp64 CPU oracle
+timed on this host on the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload flux]
 """
@@ -46,6 +48,15 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, AMD published
 MALL_BYTES = 256 << 20        # Infinity Cache
 CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches x 64 channels
 
+# HBM bytes per launch of the FLUX attention kernel from two rocprofv3 --pmc
+# passes (FETCH_SIZE, WRITE_SIZE; profiles/flux_attention_hbm_counters.md),
+# each scaled by what the counter reads for a device copy of known size.
+# Valid only for the kernel source they were taken on (SHA-256 below); any
+# change to that file reports traffic as null until the counters are re-taken.
+ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
+ATTN_TRAFFIC = {"src_sha256": "4e76bf22a6a106cf902c72c12589c4f856df1a585fda1401a48f702869e09bf2",
+                "workload": "flux", "fetch_bytes": 52_214_784, "write_bytes": 14_428_416}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -55,6 +66,7 @@ def parse():
     ap.add_argument("--workload", default="flux", choices=["flux", "qwen_u4", "qwen_u5", "wan"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true", help="skip the side permute / merge measurements")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config attention timings")
     return ap.parse_args()
 
 
@@ -87,23 +99,20 @@ class Step:
             n += t.numel() * t.element_size()
         return n
 
-    def run(self, sa, rank, ev=None):
-        """Enqueue one step; ev: optional dict name -> (start, end) events."""
+    def run(self, sa, rank, only=None):
+        """Enqueue one step (or only its kernel `only`)."""
         S2H, H2S = sa.DIT_SEQ_TO_HEAD, sa.DIT_HEAD_TO_SEQ
-
-        def timed(name, fn):
-            if ev is not None:
-                ev[name][0].record()
-            fn()
-            if ev is not None:
-                ev[name][1].record()
-
-        timed("A1_pack_qkv", lambda: sa.dit_ulysses_pack(self.L3, S2H, rank, self.shard, send=self.send3))
-        timed("A3_unpack_qkv", lambda: sa.dit_ulysses_unpack(self.L3, S2H, rank, self.send3, out=self.qkv))
-        timed("B_attention", lambda: sa.dit_attn_fwd(*self.qkv, o=self.o, lse=self.lse, scale=self.w.scale))
-        timed("D_pack_o", lambda: sa.dit_ulysses_pack(self.L1, H2S, rank, [self.o], send=self.send1))
-        timed("E_unpack_o", lambda: sa.dit_ulysses_unpack(self.L1, H2S, rank, self.send1, out=[self.out]))
-        timed("F_cfg", lambda: sa.dit_cfg_combine(self.u, self.c, 4.0, out=self.guided))
+        launches = (
+            ("A1_pack_qkv", lambda: sa.dit_ulysses_pack(self.L3, S2H, rank, self.shard, send=self.send3)),
+            ("A3_unpack_qkv", lambda: sa.dit_ulysses_unpack(self.L3, S2H, rank, self.send3, out=self.qkv)),
+            ("B_attention", lambda: sa.dit_attn_fwd(*self.qkv, o=self.o, lse=self.lse, scale=self.w.scale)),
+            ("D_pack_o", lambda: sa.dit_ulysses_pack(self.L1, H2S, rank, [self.o], send=self.send1)),
+            ("E_unpack_o", lambda: sa.dit_ulysses_unpack(self.L1, H2S, rank, self.send1, out=[self.out])),
+            ("F_cfg", lambda: sa.dit_cfg_combine(self.u, self.c, 4.0, out=self.guided)),
+        )
+        for name, fn in launches:
+            if only is None or only == name:
+                fn()
 
 
 def kernel_bytes(step):
@@ -179,6 +188,110 @@ def side_measurements(torch, sa, workloads, reps=20):
     return res
 
 
+def attention_configs(torch, sa, workloads, reps=10):
+    """Attention (and its permutes) at every DiT shard shape: TFLOP/s and
+    fraction of the bf16 MFMA peak, median of `reps` launches."""
+    res = {}
+
+    def dev_randn(shape, seed):
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    def attn_entry(w, us, note=None):
+        fl = w.attn_flop()
+        d = {"shape_q": [w.B, w.Sq, w.H, w.D], "Skv": w.Skv, "flop": fl, "us": round(us, 2),
+             "TFLOP/s": round(fl / us / 1e6, 1), "frac_mfma_peak": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+        if note:
+            d["note"] = note
+        return d
+
+    for name in ("flux", "qwen_u4", "qwen_u5", "wan"):
+        w = workloads.WORKLOADS[name]
+        q = dev_randn((w.B, w.Sq, w.H, w.D), 1)
+        k = dev_randn((w.B, w.Skv, w.H, w.D), 2)
+        v = dev_randn((w.B, w.Skv, w.H, w.D), 3)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+        n = reps if name != "wan" else max(3, reps // 3)
+        us = _time_launches(torch, lambda i: sa.dit_attn_fwd(q, k, v, o=o, lse=lse, scale=w.scale), n)
+        note = None
+        if name == "qwen_u5":
+            note = (f"5 heads incl. the zero pad head; useful TFLOP/s (x24/25) = "
+                    f"{w.attn_flop() / us / 1e6 * 24 / 25:.1f}")
+        res[f"attn_{name}"] = attn_entry(w, us, note)
+        del q, k, v, o, lse
+
+    # ring shard: 4 K/V chunks of 4096 keys, each followed by a merge into the
+    # bf16 accumulator, against one unchunked call over all 16384 keys
+    rw = workloads.WORKLOADS["ring"]
+    q = dev_randn((rw.B, rw.Sq, rw.H, rw.D), 4)
+    k = dev_randn((rw.B, rw.Skv, rw.H, rw.D), 5)
+    v = dev_randn((rw.B, rw.Skv, rw.H, rw.D), 6)
+    chunk = rw.Skv // rw.R
+    o_acc = torch.empty_like(q)
+    lse_acc = torch.empty((rw.B, rw.H, rw.Sq), dtype=torch.float32, device="cuda")
+    o_part = torch.empty_like(q)
+    lse_part = torch.empty_like(lse_acc)
+    order = [(0 - t) % rw.R for t in range(rw.R)]
+
+    def ring(i):
+        for t, c in enumerate(order):
+            kc, vc = k[:, c * chunk:(c + 1) * chunk], v[:, c * chunk:(c + 1) * chunk]
+            if t == 0:
+                sa.dit_attn_fwd(q, kc, vc, o=o_acc, lse=lse_acc, scale=rw.scale)
+            else:
+                sa.dit_attn_fwd(q, kc, vc, o=o_part, lse=lse_part, scale=rw.scale)
+                sa.dit_attn_merge(o_acc, lse_acc, o_part, lse_part)
+
+    us = _time_launches(torch, ring, reps)
+    fl = rw.attn_flop()
+    res["attn_ring_chunked_e2e"] = {
+        "chunks": rw.R, "merges": rw.R - 1, "flop": fl, "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
+        "frac_mfma_peak": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4),
+        "note": "4 x attention [1,4096,24,128] x 4096 keys + 3 bf16 merges, hop order 0,3,2,1"}
+    kc, vc = k[:, :chunk], v[:, :chunk]
+    us = _time_launches(torch, lambda i: sa.dit_attn_fwd(q, kc, vc, o=o_part, lse=lse_part, scale=rw.scale),
+                        reps)
+    res["attn_ring_chunk"] = {"flop": fl // rw.R, "us": round(us, 2), "TFLOP/s": round(fl / rw.R / us / 1e6, 1),
+                              "frac_mfma_peak": round(fl / rw.R / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    us = _time_launches(torch, lambda i: sa.dit_attn_fwd(q, k, v, o=o_acc, lse=lse_acc, scale=rw.scale), reps)
+    res["attn_ring_unchunked"] = {"flop": fl, "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
+                                  "frac_mfma_peak": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, o_acc, o_part
+
+    # Qwen Ulysses QKV pack / unpack at U=4 (sequence pad) and U=5 (head pad)
+    for name in ("qwen_u4", "qwen_u5"):
+        w = workloads.WORKLOADS[name]
+        L = sa.dit_a2a_layout_init(w.B, w.S, w.H_total, w.D, w.U, 1, 3)
+        rank = w.U - 1  # the rank that holds the pad rows / pad head
+        shard_elems = w.B * L.S_loc * w.H_total * w.D
+        send_elems = w.U * L.elems_per_peer
+        out_elems = w.B * w.S * L.H_loc * w.D
+        shard = [torch.empty(shard_elems, dtype=torch.bfloat16, device="cuda").view(w.B, L.S_loc, w.H_total, w.D)
+                 for _ in range(3)]
+        for t in shard:
+            t.normal_()
+        send = torch.empty((w.U, 3, w.B, L.S_loc, L.H_loc, w.D), dtype=torch.bfloat16, device="cuda")
+        outs = [torch.empty((w.B, w.S, L.H_loc, w.D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+        real_rows = min(L.S_loc, w.S - rank * L.S_loc)
+        pack_bytes = 2 * (3 * w.B * real_rows * w.H_total * w.D + send_elems)
+        unpack_bytes = 2 * (send_elems + 3 * out_elems)
+        us = _time_launches(torch, lambda i: sa.dit_ulysses_pack(L, sa.DIT_SEQ_TO_HEAD, rank, shard, send=send),
+                            reps)
+        res[f"{name}_pack_qkv"] = {"rank": rank, "bytes": pack_bytes, "us": round(us, 2),
+                                   "GB/s": round(pack_bytes / us / 1e3, 1),
+                                   "frac_hbm_peak": round(pack_bytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                                   "note": "MALL-warm: one buffer set"}
+        us = _time_launches(torch, lambda i: sa.dit_ulysses_unpack(L, sa.DIT_SEQ_TO_HEAD, rank, send, out=outs),
+                            reps)
+        res[f"{name}_unpack_qkv"] = {"rank": rank, "bytes": unpack_bytes, "us": round(us, 2),
+                                     "GB/s": round(unpack_bytes / us / 1e3, 1),
+                                     "frac_hbm_peak": round(unpack_bytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                                     "note": "MALL-warm: one buffer set"}
+        del shard, send, outs
+    return res
+
+
 def _time_launches(torch, fn, reps):
     for i in range(3):
         fn(i)
@@ -191,6 +304,18 @@ def _time_launches(torch, fn, reps):
     torch.cuda.synchronize()
     times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
     return times[len(times) // 2]
+
+
+def attn_traffic(w):
+    """Counter-measured HBM bytes per attention launch, or None when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    if w.name != ATTN_TRAFFIC["workload"]:
+        return None
+    with open(ATTN_SRC, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != ATTN_TRAFFIC["src_sha256"]:
+            return None
+    return ATTN_TRAFFIC["fetch_bytes"] + ATTN_TRAFFIC["write_bytes"]
 
 
 def cpu_baseline(w, attn_flop):
@@ -246,24 +371,38 @@ def main():
         steps[i % n_sets].run(sa, rank)
     torch.cuda.synchronize()
 
-    # timed region: K steps, events around every kernel on the launch stream
-    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
-          for _ in range(args.steps)]
+    # timed region: K steps bracketed by two HIP events on the launch stream.
+    # No events between kernels: each event record idles the stream for
+    # several microseconds, which would stretch the step.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        steps[i % n_sets].run(sa, rank, ev[i])
+        steps[i % n_sets].run(sa, rank)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
-    per_kernel = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in ev) / args.steps * 1e3 for n in names}
+
+    # per-kernel average launch duration: each kernel of the step launched K
+    # times back to back over the rotated input sets, the run bracketed by
+    # two events on the same stream (region time / K)
+    per_kernel = {}
+    for n in names:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        steps[0].run(sa, rank, only=n)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(args.steps):
+            steps[i % n_sets].run(sa, rank, only=n)
+        b.record()
+        torch.cuda.synchronize()
+        per_kernel[n] = a.elapsed_time(b) / args.steps * 1e3
+    attn_us = per_kernel["B_attention"]
 
     attn_flop = w.attn_flop()
     value = attn_flop / (ms_per_step * 1e-3) / 1e12
-    attn_us = per_kernel["B_attention"]
     achieved = attn_flop / (attn_us * 1e-6) / 1e12
     kb = kernel_bytes(one)
     kernels = {}
@@ -296,12 +435,14 @@ def main():
                    "input_sets_rotated": n_sets, "wall_s_timed": round(wall, 3)},
         "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic(w),
                      "algorithmic_flop_per_launch": attn_flop, "avg_launch_us": round(attn_us, 2)},
         "kernels": kernels,
     }
     if not args.no_side:
         result["side"] = side_measurements(torch, sa, workloads)
+    if not args.no_configs:
+        result["configs"] = attention_configs(torch, sa, workloads)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, attn_flop)
     print(json.dumps(result), flush=True)

@@ -19,9 +19,10 @@
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers to contiguous row-major tensors,
- *     owned by the caller.  The library never allocates, frees or retains
- *     device memory and keeps no state between calls (thread-safe and
- *     reentrant; only the per-thread error text is stored).
+ *     owned by the caller; the library never frees or retains them.  The
+ *     only library-owned device memory is dit_attn_fwd's per-(device,
+ *     stream) workspace (see there).  Thread-safe; the per-thread error
+ *     text is the only other state.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*,
  *     NULL = the default stream) and never synchronizes.
  *   - All validation happens before any launch; on an error nothing is
@@ -173,9 +174,19 @@ dit_status_t dit_ulysses_unpack(const dit_a2a_layout* layout, dit_a2a_dir_t dir,
  * D in {64, 128}.
  * Sq == 0 or B == 0 or H == 0: no-op.  Skv == 0: O = 0 and LSE = -inf (the
  *   identity of dit_attn_merge).
- * No aliasing between inputs and outputs.  Deterministic (no atomics).
+ * No aliasing between inputs and outputs.  Deterministic: a repeated call
+ *   on the same device returns bitwise identical O and LSE.
+ * Workspace: the bf16 path may cut query tiles into key chunks merged on
+ *   the GPU; their partial results and per-tile arrival counters live in a
+ *   workspace the library allocates (hipMalloc) on the first call on each
+ *   (device, stream) that needs it, zero-fills on `stream`, grows when a
+ *   larger call comes (after synchronizing `stream`) and keeps until the
+ *   process ends (at most about 35 MB per stream on a 256-CU device).
+ *   Calls on different streams never share it.  A first call on a stream
+ *   therefore allocates and cannot be captured into a graph.
  * Errors: INVALID_ARGUMENT (null pointer of a non-empty tensor, negative
- * size, bad scale or dtype); UNSUPPORTED (D, dtype pair, alignment); HIP.
+ * size, bad scale or dtype); UNSUPPORTED (D, dtype pair, alignment); HIP
+ * (including a failed workspace allocation).
  */
 dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                           int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
