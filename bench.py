@@ -20,6 +20,9 @@ Ulysses degree 2, ring degree 1):
 the measured step time (K steps bracketed by two HIP events on the launch
 stream).  Inputs are resident in HBM before timing; input sets rotate so
 that successive steps do not find their data in the 256 MB Infinity Cache.
+Before the warm-up steps, untimed steps run for --clock-warmup-s seconds:
+the GPU clock needs a few hundred milliseconds of sustained work to leave
+its idle level, and a denoising loop runs its attention blocks for seconds.
 The JSON line also carries the attention kernel's roofline (its average
 launch duration: K back-to-back launches bracketed by events), per-kernel
 times, attention at every DiT shard shape, side measurements of the headline
@@ -67,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true", help="skip the side permute / merge measurements")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config attention timings")
+    ap.add_argument("--clock-warmup-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up steps, to bring the GPU clock up")
     return ap.parse_args()
 
 
@@ -292,10 +297,24 @@ def attention_configs(torch, sa, workloads, reps=10):
     return res
 
 
-def _time_launches(torch, fn, reps):
-    for i in range(3):
-        fn(i)
-    torch.cuda.synchronize()
+def warm_clock(torch, fn, seconds):
+    """Keep the GPU busy with `fn` for about `seconds` of wall time.  The
+    shader clock ramps up over a few hundred milliseconds of sustained work
+    (measured with s_memtime / s_memrealtime: ~1.7 GHz in the first
+    milliseconds after idle, ~2.0-2.2 GHz once warm); a DiT denoising loop
+    runs its attention blocks back to back for seconds, so timings are taken
+    at the warm clock."""
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
+def _time_launches(torch, fn, reps, warm_s=0.15):
+    warm_clock(torch, fn, warm_s)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i, (a, b) in enumerate(evs):
         a.record()
@@ -367,6 +386,7 @@ def main():
     names = ["A1_pack_qkv", "A3_unpack_qkv", "B_attention", "D_pack_o", "E_unpack_o", "F_cfg"]
     rank = 0
 
+    warm_clock(torch, lambda i: steps[i % n_sets].run(sa, rank), args.clock_warmup_s)
     for i in range(args.warmup):
         steps[i % n_sets].run(sa, rank)
     torch.cuda.synchronize()
@@ -391,8 +411,7 @@ def main():
     per_kernel = {}
     for n in names:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        steps[0].run(sa, rank, only=n)
-        torch.cuda.synchronize()
+        warm_clock(torch, lambda i: steps[i % n_sets].run(sa, rank, only=n), 0.1)
         a.record()
         for i in range(args.steps):
             steps[i % n_sets].run(sa, rank, only=n)
@@ -432,7 +451,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.note}", "B": w.B, "S": w.S, "H_total": w.H_total,
                    "H_rank": w.H, "D": w.D, "ulysses": w.U, "ring": w.R, "rank": rank,
-                   "input_sets_rotated": n_sets, "wall_s_timed": round(wall, 3)},
+                   "input_sets_rotated": n_sets, "wall_s_timed": round(wall, 3),
+                   "clock_warmup_s": args.clock_warmup_s},
         "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic(w),
