@@ -254,6 +254,20 @@ def attention_configs(torch, sa, workloads, reps=10):
         "chunks": rw.R, "merges": rw.R - 1, "flop": fl, "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
         "frac_mfma_peak": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4),
         "note": "4 x attention [1,4096,24,128] x 4096 keys + 3 bf16 merges, hop order 0,3,2,1"}
+
+    def ring_fused(i):
+        for t, c in enumerate(order):
+            kc, vc = k[:, c * chunk:(c + 1) * chunk], v[:, c * chunk:(c + 1) * chunk]
+            if t == 0:
+                sa.dit_attn_fwd(q, kc, vc, o=o_acc, lse=lse_acc, scale=rw.scale)
+            else:
+                sa.dit_attn_fwd_merge(q, kc, vc, o_acc, lse_acc, scale=rw.scale)
+
+    us = _time_launches(torch, ring_fused, reps)
+    res["attn_ring_fused_e2e"] = {
+        "chunks": rw.R, "flop": fl, "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
+        "frac_mfma_peak": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4),
+        "note": "hop 0 with dit_attn_fwd, hops 1-3 with dit_attn_fwd_merge (merge in the epilogue)"}
     kc, vc = k[:, :chunk], v[:, :chunk]
     us = _time_launches(torch, lambda i: sa.dit_attn_fwd(q, kc, vc, o=o_part, lse=lse_part, scale=rw.scale),
                         reps)

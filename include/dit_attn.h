@@ -9,6 +9,8 @@
  *   dit_attn_fwd                           attention with per-row LSE
  *   dit_attn_merge                         online-softmax merge of partial
  *                                          results (ring hops)
+ *   dit_attn_fwd_merge                     one ring hop: attention of a K/V
+ *                                          chunk merged into the accumulator
  *   dit_cfg_combine                        classifier-free guidance combine
  *
  * Shapes follow SGLang Diffusion "Parallelism Overview" ("What happens to
@@ -212,6 +214,31 @@ dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, 
 dit_status_t dit_attn_merge(void* o_acc, float* lse_acc, const void* o_part,
                             const float* lse_part, int32_t B, int32_t Sq, int32_t H, int32_t D,
                             dit_dtype_t o_dtype, void* stream);
+
+/*
+ * One ring hop in one call: attention of q over this K/V chunk merged into
+ * the running accumulator (SGLang "Parallelism Overview": the ring keeps Q
+ * in place while K/V chunks rotate, and each hop's partial result is folded
+ * into the running one with the online-softmax rule through its LSE).  The
+ * result equals dit_attn_fwd into a temporary followed by dit_attn_merge,
+ * up to rounding (the chunk's O is not rounded to acc_dtype before the
+ * merge), without the temporary's HBM round trip.
+ *
+ * q, k, v, scale, in_dtype: as dit_attn_fwd.
+ * o_acc: [B, Sq, H, D] in acc_dtype (in_dtype, or DIT_F32 for bf16 input);
+ * lse_acc: [B, H, Sq] fp32, required.  Both are read and written in place.
+ *   A row whose lse_acc is -inf holds no keys yet: the call overwrites it
+ *   with this chunk's result (so an accumulator set to the identity
+ *   O = 0, LSE = -inf starts the hop loop).
+ * Skv == 0: the chunk is empty, the accumulator is left unchanged.
+ * No aliasing between q/k/v and the accumulator.  Deterministic.
+ * Workspace: as dit_attn_fwd.
+ * Errors: as dit_attn_fwd; INVALID_ARGUMENT also when lse_acc is NULL.
+ */
+dit_status_t dit_attn_fwd_merge(const void* q, const void* k, const void* v, void* o_acc,
+                                float* lse_acc, int32_t B, int32_t Sq, int32_t Skv, int32_t H,
+                                int32_t D, float scale, dit_dtype_t in_dtype, dit_dtype_t acc_dtype,
+                                void* stream);
 
 /*
  * Classifier-free guidance combine (edge-dit.cpp "Parallel execution", CFG

@@ -27,7 +27,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "dit_abi_version", "dit_a2a_layout_init", "dit_ulysses_pack", "dit_ulysses_unpack",
-    "dit_attn_fwd", "dit_attn_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
+    "dit_attn_fwd", "dit_attn_merge", "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
 
@@ -157,6 +157,26 @@ def dit_attn_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
     check(lib().dit_attn_merge(_dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc"), _dev(o_part, "o_part"),
                                _dev(lse_part, "lse_part"), B, Sq, H, D, _dtype_code(o_acc.dtype),
                                _stream(stream)), "dit_attn_merge")
+    return o_acc, lse_acc
+
+
+def dit_attn_fwd_merge(q, k, v, o_acc, lse_acc, scale=None, stream=None):
+    """One ring hop: attention of q over the chunk (k, v) merged in place
+    into the accumulator (o_acc [B, Sq, H, D], lse_acc [B, H, Sq] fp32)."""
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if tuple(k.shape) != (B, Skv, H, D) or tuple(v.shape) != (B, Skv, H, D):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if tuple(o_acc.shape) != (B, Sq, H, D) or tuple(lse_acc.shape) != (B, H, Sq):
+        raise ValueError("accumulator must be o [B, Sq, H, D] and lse [B, H, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    check(lib().dit_attn_fwd_merge(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o_acc, "o_acc"),
+                                   _dev(lse_acc, "lse_acc"), B, Sq, Skv, H, D, float(scale),
+                                   _dtype_code(q.dtype), _dtype_code(o_acc.dtype), _stream(stream)),
+          "dit_attn_fwd_merge")
     return o_acc, lse_acc
 
 

@@ -35,6 +35,7 @@ EXPORTS = (
     "dit_ulysses_unpack",
     "dit_attn_fwd",
     "dit_attn_merge",
+    "dit_attn_fwd_merge",
     "dit_cfg_combine",
 )
 
@@ -89,6 +90,9 @@ def _declare(lib):
                                                                      ctypes.c_int, _P]
     lib.dit_attn_merge.restype = ctypes.c_int
     lib.dit_attn_merge.argtypes = [_P, _P, _P, _P] + [_I32] * 4 + [ctypes.c_int, _P]
+    lib.dit_attn_fwd_merge.restype = ctypes.c_int
+    lib.dit_attn_fwd_merge.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                           ctypes.c_int, _P]
     lib.dit_cfg_combine.restype = ctypes.c_int
     lib.dit_cfg_combine.argtypes = [_P, _P, _P, ctypes.c_int64, ctypes.c_float, ctypes.c_int, _P]
 

@@ -117,7 +117,7 @@ constexpr size_t slot_floats() {
   return (size_t)kWaves * 64 * (D / 2 + 2);
 }
 
-template <int D, bool kOutF32>
+template <int D, bool kOutF32, bool kMerge>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   constexpr int ROWB = D * 2;                 // bytes of one K/V row
   constexpr int BLKB = kBN * ROWB;            // bytes of one K or V block
@@ -357,29 +357,65 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     }
 
     // ---- normalise and store O and LSE (lane: one query, 16 dims per tile) --
+    // Normalise and store O and LSE.  With kMerge, (O, LSE) already hold a
+    // partial result over other keys (a previous ring hop) and this chunk is
+    // merged into them by the online-softmax rule: with L_c = this chunk's
+    // LSE, m = max(L_a, L_c) and w_x = exp(L_x - m),
+    //   O = (w_a O_a + w_c O_c) / (w_a + w_c),  LSE = m + ln(w_a + w_c);
+    // an accumulator with L_a = -inf holds no keys and is replaced.  The two
+    // lanes of a row read the old LSE before the first of them writes it
+    // (same wave, program order).
     auto store_out = [&](const f32x16 (&acc)[DT], float m_ref, float l_lane) __attribute__((always_inline)) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       const float ltot = l_lane + __shfl_xor(l_lane, 32);
       if (!q_ok) return;
-      const float inv = 1.0f / ltot;
       const size_t orow = ((size_t)b * p.Sq + q_row) * rs + (size_t)h * D;
+      const size_t lse_idx = ((size_t)b * p.H + h) * p.Sq + q_row;
+      const float l_c = m_ref * p.scale + __logf(ltot);
+      float cc = 1.0f / ltot, ca = 0.0f, l_new = l_c;
+      if constexpr (kMerge) {
+        const float l_a = p.lse[lse_idx];
+        if (l_a != -INFINITY) {
+          const float m = fmaxf(l_a, l_c);
+          const float wa = __expf(l_a - m), wc = __expf(l_c - m);
+          const float den = wa + wc;
+          ca = wa / den;
+          cc = wc / (den * ltot);
+          l_new = m + __logf(den);
+        }
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int d = dt * 32 + 8 * u + 4 * g;
-          const float o0 = acc[dt][4 * u + 0] * inv, o1 = acc[dt][4 * u + 1] * inv;
-          const float o2 = acc[dt][4 * u + 2] * inv, o3 = acc[dt][4 * u + 3] * inv;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[dt][4 * u + e] * cc;
+          if constexpr (kMerge) {
+            if (ca != 0.0f) {
+              float prev[4];
+              if constexpr (kOutF32) {
+                const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(p.o) + orow + d);
+                prev[0] = x.x; prev[1] = x.y; prev[2] = x.z; prev[3] = x.w;
+              } else {
+                const bf16x4 x = *reinterpret_cast<const bf16x4*>(static_cast<const uint16_t*>(p.o) + orow + d);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) prev[e] = (float)x[e];
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(ca, prev[e], o[e]);
+            }
+          }
           if constexpr (kOutF32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.o) + orow + d) = make_float4(o0, o1, o2, o3);
+            *reinterpret_cast<float4*>(static_cast<float*>(p.o) + orow + d) = make_float4(o[0], o[1], o[2], o[3]);
           } else {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
             bf16x4 w;
-            w[0] = (__bf16)o0; w[1] = (__bf16)o1; w[2] = (__bf16)o2; w[3] = (__bf16)o3;
+            w[0] = (__bf16)o[0]; w[1] = (__bf16)o[1]; w[2] = (__bf16)o[2]; w[3] = (__bf16)o[3];
             *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.o) + orow + d) = w;
           }
         }
-      if (p.lse != nullptr && g == 0)
-        p.lse[((size_t)b * p.H + h) * p.Sq + q_row] = m_ref * p.scale + __logf(ltot);
+      if (p.lse != nullptr && g == 0) p.lse[lse_idx] = l_new;
     };
 
     if (whole) {
@@ -458,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   }
 }
 
-template <int D, bool kOutF32>
+template <int D, bool kOutF32, bool kMerge>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   Params p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -479,14 +515,14 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   // the last round would leave many of them idle, its tiles are instead cut
   // into `split` key chunks, one workgroup each, merged by the online-softmax
   // rule.
-  static int occupancy[kMaxDevices] = {};
+  static int occupancy[kMaxDevices] = {};  // per instantiation
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   if (occupancy[dev] == 0) {
     int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, kOutF32>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, kOutF32, kMerge>, kThreads, 0);
     if (e != hipSuccess) return e;
     occupancy[dev] = per_cu > 0 ? per_cu : 1;
   }
@@ -508,15 +544,19 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   p.cnt = static_cast<int32_t*>(cnt);
   p.part = static_cast<float*>(part);
-  attn_bf16_kernel<D, kOutF32><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  attn_bf16_kernel<D, kOutF32, kMerge><<<(unsigned)grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
-  if (a.D == 64) return a.o_f32 ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
-  return a.o_f32 ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+  if (a.merge) {
+    if (a.D == 64) return a.o_f32 ? launch_t<64, true, true>(a, stream) : launch_t<64, false, true>(a, stream);
+    return a.o_f32 ? launch_t<128, true, true>(a, stream) : launch_t<128, false, true>(a, stream);
+  }
+  if (a.D == 64) return a.o_f32 ? launch_t<64, true, false>(a, stream) : launch_t<64, false, false>(a, stream);
+  return a.o_f32 ? launch_t<128, true, false>(a, stream) : launch_t<128, false, false>(a, stream);
 }
 
 }  // namespace dit

@@ -19,7 +19,7 @@ constexpr int kRows = 64;   // query rows per workgroup
 constexpr int kKeys = 32;   // keys per LDS tile
 constexpr int kThreads = 2 * kRows;  // two lanes per row, each owning D/2 columns
 
-template <int D>
+template <int D, bool kMerge>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const float* __restrict__ q,
                                                             const float* __restrict__ k,
                                                             const float* __restrict__ v,
@@ -81,19 +81,46 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const float* __restr
     m = mn;
   }
   if (!row_ok) return;
-  const float inv = 1.0f / l;
   float* op = o + ((size_t)b * Sq + i) * row_stride + (size_t)h * D + half * DH;
+  const size_t lse_idx = ((size_t)b * H + h) * Sq + i;
+  const float l_c = m + logf(l);
+  float cc = 1.0f / l, ca = 0.0f, l_new = l_c;
+  if constexpr (kMerge) {
+    // merge into the partial result already in (o, lse): online-softmax
+    // rule, an accumulator with LSE = -inf is replaced; both lanes of the
+    // row read the old LSE before lane 0 writes it (same wave)
+    const float l_a = lse[lse_idx];
+    if (l_a != -INFINITY) {
+      const float mm = fmaxf(l_a, l_c);
+      const float wa = expf(l_a - mm), wc = expf(l_c - mm);
+      const float den = wa + wc;
+      ca = wa / den;
+      cc = wc / (den * l);
+      l_new = mm + logf(den);
+    }
+  }
+  // an empty accumulator (ca = 0) is never read: it may hold anything
+  const bool use_prev = kMerge && ca != 0.0f;
 #pragma unroll
-  for (int d = 0; d < DH; ++d) op[d] = acc[d] * inv;
-  if (lse && half == 0) lse[((size_t)b * H + h) * Sq + i] = m + logf(l);
+  for (int d = 0; d < DH; ++d) {
+    float r = acc[d] * cc;
+    if (use_prev) r = __builtin_fmaf(ca, op[d], r);
+    op[d] = r;
+  }
+  if (lse && half == 0) lse[lse_idx] = l_new;
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   dim3 grid((a.Sq + kRows - 1) / kRows, a.H, a.B);
-  attn_f32_kernel<D><<<grid, kThreads, 0, stream>>>(
-      static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-      static_cast<float*>(a.o), a.lse, a.Sq, a.Skv, a.H, a.scale);
+  if (a.merge)
+    attn_f32_kernel<D, true><<<grid, kThreads, 0, stream>>>(
+        static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
+        static_cast<float*>(a.o), a.lse, a.Sq, a.Skv, a.H, a.scale);
+  else
+    attn_f32_kernel<D, false><<<grid, kThreads, 0, stream>>>(
+        static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
+        static_cast<float*>(a.o), a.lse, a.Sq, a.Skv, a.H, a.scale);
   return hipGetLastError();
 }
 

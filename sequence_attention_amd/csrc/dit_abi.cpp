@@ -213,9 +213,13 @@ dit_status_t dit_ulysses_unpack(const dit_a2a_layout* layout, dit_a2a_dir_t dir,
   return run_permute(layout, (int)dir, rank, false, nullptr, recv_buf, out_planes, nullptr, stream);
 }
 
-dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                          int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
-                          dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* stream) {
+namespace {
+
+// dit_attn_fwd and dit_attn_fwd_merge: one validation path; `merge` makes
+// (o, lse) an accumulator that this call merges into.
+dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                       int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale, dit_dtype_t in_dtype,
+                       dit_dtype_t o_dtype, void* stream, bool merge) {
   if (B < 0 || Sq < 0 || Skv < 0 || H < 0 || D < 0)
     return fail(DIT_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Skv=%d H=%d D=%d)", B, Sq, Skv,
                 H, D);
@@ -234,6 +238,7 @@ dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, 
     return DIT_OK;
   }
   if (q == nullptr || o == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "q or o is NULL");
+  if (merge && lse == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "the merge needs the accumulator's LSE");
   if (Skv > 0 && (k == nullptr || v == nullptr))
     return fail(DIT_ERR_INVALID_ARGUMENT, "k or v is NULL");
   if (!aligned(q, 16) || !aligned(o, 16) || (Skv > 0 && (!aligned(k, 16) || !aligned(v, 16))))
@@ -256,8 +261,13 @@ dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   if (in_dtype == DIT_F32 && (H > 65535 || B > 65535))
     return fail(DIT_ERR_UNSUPPORTED, "fp32 path limits B and H to 65535");
 
+  if (merge && Skv == 0) {  // an empty chunk is the merge identity
+    clear_error();
+    return DIT_OK;
+  }
   dit::AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.merge = merge;
   a.B = B; a.Sq = Sq; a.Skv = Skv; a.H = H; a.D = D;
   a.scale = scale;
   a.o_f32 = (o_dtype == DIT_F32);
@@ -268,6 +278,21 @@ dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   const dit_status_t st = hip_status(e, "attention launch");
   if (st == DIT_OK) clear_error();
   return st;
+}
+
+}  // namespace
+
+dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
+                          dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* stream) {
+  return attn_call(q, k, v, o, lse, B, Sq, Skv, H, D, scale, in_dtype, o_dtype, stream, false);
+}
+
+dit_status_t dit_attn_fwd_merge(const void* q, const void* k, const void* v, void* o_acc,
+                                float* lse_acc, int32_t B, int32_t Sq, int32_t Skv, int32_t H,
+                                int32_t D, float scale, dit_dtype_t in_dtype, dit_dtype_t acc_dtype,
+                                void* stream) {
+  return attn_call(q, k, v, o_acc, lse_acc, B, Sq, Skv, H, D, scale, in_dtype, acc_dtype, stream, true);
 }
 
 dit_status_t dit_attn_merge(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part,

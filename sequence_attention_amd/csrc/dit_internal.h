@@ -84,6 +84,7 @@ struct AttnArgs {
   int32_t B, Sq, Skv, H, D;
   float scale;
   bool o_f32;  // bf16 input only: write O as fp32
+  bool merge = false;  // o / lse hold a partial result to merge this call into
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);

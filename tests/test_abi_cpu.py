@@ -167,6 +167,32 @@ def test_attn_empty_is_a_no_op(lib):
     assert lib.dit_last_error().decode() == ""
 
 
+def _attn_merge(lib, q=A, k=A + 2**24, v=A + 2**25, o=A + 2**26, lse=A + 2**27, B=1, Sq=128, Skv=128,
+                H=2, D=64, scale=0.125, din=0, dacc=0):
+    return lib.dit_attn_fwd_merge(P(q), P(k), P(v), P(o), P(lse), B, Sq, Skv, H, D, scale, din, dacc,
+                                  NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), INV), (dict(din=7), INV), (dict(scale=0.0), INV), (dict(scale=math.nan), INV),
+    (dict(din=1, dacc=1), UNS), (dict(D=96), UNS), (dict(din=2, dacc=0), UNS),
+    (dict(q=0), INV), (dict(o=0), INV), (dict(k=0), INV),
+    (dict(lse=0), INV),                             # the accumulator's LSE is required
+    (dict(q=A + 8), UNS), (dict(lse=A + 2**27 + 2), UNS),
+    (dict(o=A + 1024), INV),                        # accumulator overlaps q
+])
+def test_attn_fwd_merge_rejects(lib, kw, code):
+    assert _attn_merge(lib, **kw) == code, lib.dit_last_error()
+    assert lib.dit_last_error().decode() != ""
+
+
+def test_attn_fwd_merge_empty_chunk_is_a_no_op(lib):
+    # Skv = 0 is the merge identity: nothing is launched, no pointer is used
+    assert _attn_merge(lib, k=0, v=0, Skv=0) == 0
+    assert _attn_merge(lib, q=0, k=0, v=0, o=0, lse=0, Sq=0) == 0
+    assert lib.dit_last_error().decode() == ""
+
+
 def _merge(lib, oa=A, la=A + 2**24, op=A + 2**25, lp=A + 2**26, B=1, Sq=16, H=2, D=64, dt=0):
     return lib.dit_attn_merge(P(oa), P(la), P(op), P(lp), B, Sq, H, D, dt, NULL)
 

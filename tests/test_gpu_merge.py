@@ -139,3 +139,103 @@ def test_single_chunk_ring_is_plain_attention_bitwise():
     o, l = sa.dit_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(acc, o) and torch.equal(acc_l, l)
+
+
+# ---- one ring hop per call: attention fused with the merge ------------------
+
+def ring_fused_on_gpu(q, k, v, scale, bounds, order, acc_dtype):
+    """The hop loop with dit_attn_fwd_merge: the accumulator starts as the
+    merge identity (O = 0, LSE = -inf) and every chunk is folded into it."""
+    B, Sq, H, D = q.shape
+    qd = q.to(DEV)
+    acc = torch.zeros((B, Sq, H, D), dtype=acc_dtype, device=DEV)
+    acc_l = torch.full((B, H, Sq), -np.inf, dtype=torch.float32, device=DEV)
+    for c in order:
+        kc = k[:, bounds[c]:bounds[c + 1]].contiguous().to(DEV)
+        vc = v[:, bounds[c]:bounds[c + 1]].contiguous().to(DEV)
+        sa.dit_attn_fwd_merge(qd, kc, vc, acc, acc_l, scale=scale)
+    torch.cuda.synchronize()
+    return acc, acc_l
+
+
+@pytest.mark.parametrize("acc_dtype", [torch.bfloat16, torch.float32])
+def test_fused_tiny_ring_vs_oracle(acc_dtype):
+    w = workloads.WORKLOADS["tiny"]
+    log(f"fused ring tiny R=2 acc {acc_dtype}")
+    q, k, v = workloads.attention_inputs(w)
+    bounds = [0, 128, 256]
+    order = oracle.ring_hop_order(2, 0)
+    acc, acc_l = ring_fused_on_gpu(q, k, v, w.scale, bounds, order, acc_dtype)
+    ro, rl = oracle.ring_attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), w.scale,
+                                   bounds, order)
+    assert max_abs(acc.float().cpu().numpy(), ro) <= 1e-2
+    assert max_abs(acc_l.cpu().numpy(), rl) <= 1e-3
+
+
+@pytest.mark.parametrize("order", [[0, 3, 2, 1], [2, 0, 3, 1]])
+def test_fused_ring_config_vs_oracle_and_unfused(order):
+    w = workloads.WORKLOADS["ring"]
+    log(f"fused ring [1,4096,24,128] x 4 chunks order {order}")
+    q, k, v = workloads.attention_inputs(w)
+    bounds = [w.Skv * c // 4 for c in range(5)]
+    acc, acc_l = ring_fused_on_gpu(q, k, v, w.scale, bounds, order, torch.bfloat16)
+    rows = np.arange(0, 4096, 61)
+    ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), w.scale, rows=rows)
+    go = acc.float().cpu().numpy()[:, rows]
+    assert max_abs(go, ro) <= 1e-2
+    assert max_abs(go, ro) / np.max(np.abs(ro)) <= 2e-2
+    assert max_abs(acc_l.cpu().numpy()[:, :, rows], rl) <= 1e-3
+    # against the unfused hop loop (attention into a temporary + merge)
+    un, un_l, _ = ring_on_gpu(q, k, v, w.scale, 4, order, torch.bfloat16)
+    assert max_abs(acc.float().cpu().numpy(), un.float().cpu().numpy()) <= 1e-2
+    assert max_abs(acc_l.cpu().numpy(), un_l.cpu().numpy()) <= 1e-3
+
+
+# uneven chunk bounds, ragged rows and head dims, split tiles in the merge path
+FUSED_RAGGED = [
+    # B, Sq, Skv, H, D, chunk bounds
+    (1, 1000, 1000, 8, 128, [0, 300, 301, 1000]),
+    (2, 130, 700, 3, 64, [0, 64, 500, 700]),
+    (1, 4000, 700, 20, 64, [0, 350, 700]),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_RAGGED)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_fused_ragged_chunks_vs_oracle(case, dtype):
+    B, Sq, Skv, H, D, bounds = case
+    log(f"fused ring ragged {dtype} {case}")
+    wl = workloads.Workload("ragged", B=B, Sq=Sq, Skv=Skv, H=H, D=D, R=len(bounds) - 1, S=Skv,
+                            H_total=H, U=1)
+    q, k, v = workloads.attention_inputs(wl, dtype=dtype, seed=Sq + Skv)
+    order = list(range(len(bounds) - 1))[::-1]
+    acc, acc_l = ring_fused_on_gpu(q, k, v, wl.scale, bounds, order, dtype)
+    rows = np.unique(np.concatenate([np.arange(0, Sq, max(1, Sq // 97)), [Sq - 1]]))
+    ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), wl.scale, rows=rows)
+    tol_o, tol_l = (1e-2, 1e-3) if dtype == torch.bfloat16 else (1e-5, 1e-5)
+    assert max_abs(acc.float().cpu().numpy()[:, rows], ro) <= tol_o
+    assert max_abs(acc_l.cpu().numpy()[:, :, rows], rl) <= tol_l
+
+
+def test_fused_empty_chunk_leaves_accumulator_bitwise():
+    oa, la = _partials(1, 300, 4, 128, torch.bfloat16, 21)
+    acc, acc_l = oa.to(DEV), la.to(DEV)
+    q = torch.randn(1, 300, 4, 128).to(torch.bfloat16).to(DEV)
+    kv = torch.zeros(1, 0, 4, 128, dtype=torch.bfloat16, device=DEV)
+    sa.dit_attn_fwd_merge(q, kv, kv, acc, acc_l)
+    torch.cuda.synchronize()
+    assert torch.equal(acc.cpu(), oa) and torch.equal(acc_l.cpu(), la)
+
+
+def test_fused_first_hop_equals_plain_attention():
+    # an identity accumulator takes the chunk's result: same O (fp32 path
+    # bitwise: the merge weights are exactly 0 and 1) and LSE
+    w = workloads.WORKLOADS["tiny"]
+    q, k, v = workloads.attention_inputs(w, dtype=torch.float32, seed=8)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, l = sa.dit_attn_fwd(qd, kd, vd, scale=w.scale)
+    acc = torch.zeros_like(o)
+    acc_l = torch.full_like(l, -np.inf)
+    sa.dit_attn_fwd_merge(qd, kd, vd, acc, acc_l, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(acc, o) and torch.equal(acc_l, l)
