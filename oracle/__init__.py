@@ -20,6 +20,10 @@ Sources (cited by page title and section):
   multiple of lcm(SP, 64) and padding exclusion ("MiniMax-H3 boundaries").
 * cache-dit, "Context Parallelism" -- head padding before / after the
   all-to-all ("Any Head Num" under UAA).
+* The receive preparation with RoPE on Q and K (edge-dit.cpp "Parallel
+  execution", Ulysses section) -- the RoPE convention is not on the pages;
+  the RoFormer rotation of adjacent dims with caller-given cos / sin tables
+  is the reading taken (see ``reference.rope``).
 
 Modules:
   oracle.reference  -- vectorised numpy fp64 definitions (the oracle proper)
@@ -39,6 +43,8 @@ from .reference import (  # noqa: F401
     a2a_layout,
     pack_seq_to_head,
     unpack_seq_to_head,
+    rope,
+    unpack_seq_to_head_rope,
     pack_head_to_seq,
     unpack_head_to_seq,
     all_to_all,

@@ -234,6 +234,35 @@ def unpack_seq_to_head(recv, L, rank):
     return [out[i] for i in range(n)]
 
 
+def rope(x, cos, sin):
+    """Rotary position embedding of a [B, S, H, D] tensor.
+
+    edge-dit.cpp "Parallel execution" (receive preparation) applies RoPE to
+    Q and K; the pages do not fix its convention.  Reading: the RoFormer
+    rotation of adjacent head-dim pairs (2i, 2i+1) by the angle of sequence
+    position t and pair i, given as tables cos, sin of shape [S, D/2]:
+      y[.., t, .., 2i]   = x[.., 2i] cos[t, i] - x[.., 2i+1] sin[t, i]
+      y[.., t, .., 2i+1] = x[.., 2i] sin[t, i] + x[.., 2i+1] cos[t, i]
+    """
+    x = _f64(x)
+    c = _f64(cos)[None, :, None, :]
+    s = _f64(sin)[None, :, None, :]
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x0 * c - x1 * s
+    y[..., 1::2] = x0 * s + x1 * c
+    return y
+
+
+def unpack_seq_to_head_rope(recv, L, rank, cos, sin):
+    """The fused receive preparation: the sequence-to-head unpack of the
+    packed Q, K, V buffer (n_planes = 3) followed by RoPE on planes 0 (Q)
+    and 1 (K) at their global sequence positions; V unchanged."""
+    assert L["n_planes"] == 3
+    q, k, v = unpack_seq_to_head(recv, L, rank)
+    return [rope(q, cos, sin), rope(k, cos, sin), _f64(v)]
+
+
 def pack_head_to_seq(in_planes, L, rank):
     """Head-to-sequence send buffer of Ulysses rank ``rank``.
 

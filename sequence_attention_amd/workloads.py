@@ -141,3 +141,14 @@ def cfg_inputs(shape=(2, 256, 256), seed: int = 0, dtype=torch.float32):
     """Stacked [uncond; cond] predictions for the CFG combine."""
     g = generator(seed)
     return randn(shape, g, dtype)
+
+
+def rope_tables(S: int, D: int, base: float = 10000.0):
+    """cos / sin tables [S, D/2] float32 of the one-axis rotary schedule
+    angle(t, i) = t * base^(-2i/D), computed in float64 and rounded once.
+    (Image and video tokens use per-axis schedules; those are different
+    table contents for the same kernel.)"""
+    t = torch.arange(S, dtype=torch.float64)[:, None]
+    i = torch.arange(D // 2, dtype=torch.float64)[None, :]
+    ang = t * torch.pow(torch.tensor(base, dtype=torch.float64), -2.0 * i / D)
+    return torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)
