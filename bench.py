@@ -170,6 +170,30 @@ def side_measurements(torch, sa, workloads, reps=20):
                 "bytes": moved, "us": round(us, 2), "GB/s": round(moved / us / 1e3, 1),
                 "frac_hbm_peak": round(moved / us / 1e3 / PEAK_HBM_GBPS, 4)}
         del bufs
+    # fused receive preparation (unpack + RoPE on Q and K) at the FLUX U=2 shape,
+    # against the plain unpack of the same buffer
+    fw = workloads.WORKLOADS["flux"]
+    L = sa.dit_a2a_layout_init(fw.B, fw.S, fw.H_total, fw.D, fw.U, 1, 3)
+    recv_bytes = fw.U * L.elems_per_peer * 2
+    plane_bytes = 3 * fw.B * fw.S * L.H_loc * fw.D * 2
+    cos, sin = workloads.rope_tables(fw.S, fw.D)
+    cos, sin = cos.to("cuda"), sin.to("cuda")
+    table_bytes = 2 * cos.numel() * 4
+    sets = max(2, math.ceil(2 * MALL_BYTES / (recv_bytes + plane_bytes)) + 1)
+    bufs = [(torch.empty((fw.U, 3, fw.B, L.S_loc, L.H_loc, fw.D), dtype=torch.bfloat16, device="cuda").normal_(),
+             [torch.empty((fw.B, fw.S, L.H_loc, fw.D), dtype=torch.bfloat16, device="cuda") for _ in range(3)])
+            for _ in range(sets)]
+    us = _time_launches(torch, lambda i: sa.dit_ulysses_unpack_rope(L, 0, bufs[i % sets][0], cos, sin,
+                                                                    out=bufs[i % sets][1]), reps)
+    moved = recv_bytes + plane_bytes + table_bytes
+    res["flux_unpack_rope_qkv"] = {"bytes": moved, "us": round(us, 2), "GB/s": round(moved / us / 1e3, 1),
+                                   "frac_hbm_peak": round(moved / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    us = _time_launches(torch, lambda i: sa.dit_ulysses_unpack(L, sa.DIT_SEQ_TO_HEAD, 0, bufs[i % sets][0],
+                                                               out=bufs[i % sets][1]), reps)
+    moved = recv_bytes + plane_bytes
+    res["flux_unpack_qkv_plain"] = {"bytes": moved, "us": round(us, 2), "GB/s": round(moved / us / 1e3, 1),
+                                    "frac_hbm_peak": round(moved / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    del bufs
     # hipMemcpy-class device copy of the same bytes, as the achievable-copy reference
     n_bytes = 2 * 96_768_000 // 2
     src = [torch.empty(n_bytes // 2, dtype=torch.bfloat16, device="cuda") for _ in range(6)]

@@ -6,6 +6,8 @@
  * call:
  *   dit_ulysses_pack / dit_ulysses_unpack  layout transforms around the
  *                                          Ulysses all-to-alls
+ *   dit_ulysses_unpack_rope                the receive-side unpack fused with
+ *                                          RoPE on Q and K
  *   dit_attn_fwd                           attention with per-row LSE
  *   dit_attn_merge                         online-softmax merge of partial
  *                                          results (ring hops)
@@ -156,6 +158,34 @@ dit_status_t dit_ulysses_pack(const dit_a2a_layout* layout, dit_a2a_dir_t dir, i
  */
 dit_status_t dit_ulysses_unpack(const dit_a2a_layout* layout, dit_a2a_dir_t dir, int32_t rank,
                                 const void* recv_buf, void* const* out_planes, void* stream);
+
+/*
+ * Fused receive preparation: the sequence-to-head unpack of the packed
+ * Q, K, V receive buffer with rotary position embedding applied to Q and K
+ * in the same pass (edge-dit.cpp "Parallel execution", Ulysses section:
+ * receive-buffer decoding, plane extraction, head-sharded layout and RoPE
+ * on Q and K in one operator).
+ *
+ * layout: as dit_ulysses_unpack with n_planes = 3 (planes Q, K, V).
+ * recv_buf: [U (source peer), 3, B, S_loc, H_loc, D]; out_planes: host
+ *   array of 3 device pointers, each [B, S, H_loc, D] (pad rows dropped).
+ * rope_cos, rope_sin: [S, D/2] fp32 tables indexed by the global sequence
+ *   position t and the pair index i; pair i of each Q and K head vector is
+ *   rotated (RoFormer convention, adjacent dims):
+ *     y[2i]   = x[2i] cos[t][i] - x[2i+1] sin[t][i]
+ *     y[2i+1] = x[2i] sin[t][i] + x[2i+1] cos[t][i]
+ *   evaluated in fp32 and rounded to the layout dtype (nearest even).  Any
+ *   angle schedule (one axis, or per-axis schedules of image and video
+ *   tokens) is expressed by the tables.  V is copied bit for bit; with
+ *   cos = 1 and sin = 0 the call equals dit_ulysses_unpack bit for bit.
+ * dtype: bf16, f16 or f32 with D * element size a multiple of 16 bytes;
+ *   all pointers 16-byte aligned.  Outputs must not overlap the inputs.
+ * Errors: INVALID_ARGUMENT (layout, rank, n_planes != 3, NULL pointers,
+ * overlap); UNSUPPORTED (head size, alignment, size limits); HIP.
+ */
+dit_status_t dit_ulysses_unpack_rope(const dit_a2a_layout* layout, int32_t rank, const void* recv_buf,
+                                     void* const* out_planes, const float* rope_cos,
+                                     const float* rope_sin, void* stream);
 
 /*
  * Non-causal attention with per-row log-sum-exp (edge-dit.cpp "Parallel

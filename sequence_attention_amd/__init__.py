@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "dit_abi_version", "dit_a2a_layout_init", "dit_ulysses_pack", "dit_ulysses_unpack",
+    "dit_ulysses_unpack_rope",
     "dit_attn_fwd", "dit_attn_merge", "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
@@ -119,6 +120,25 @@ def dit_ulysses_unpack(layout: DitA2ALayout, direction: int, rank: int, recv, ou
     arr = (ctypes.c_void_p * 3)(*[_dev(p, f"out[{i}]") for i, p in enumerate(out)])
     check(lib().dit_ulysses_unpack(ctypes.byref(layout), direction, rank, _dev(recv, "recv"), arr,
                                    _stream(stream)), "dit_ulysses_unpack")
+    return out
+
+
+def dit_ulysses_unpack_rope(layout: DitA2ALayout, rank: int, recv, rope_cos, rope_sin, out=None,
+                            stream=None):
+    """Sequence-to-head unpack of the packed Q, K, V receive buffer with RoPE
+    applied to Q and K (tables [S, D/2] fp32); returns [q, k, v], each
+    [B, S, H_loc, D]."""
+    torch = _torch()
+    if out is None:
+        shape = (layout.B, layout.S, layout.H_loc, layout.D)
+        out = [torch.empty(shape, dtype=_torch_dtype(layout.dtype), device=recv.device) for _ in range(3)]
+    out = list(out)
+    if len(out) != 3:
+        raise ValueError("expected 3 output planes (q, k, v)")
+    arr = (ctypes.c_void_p * 3)(*[_dev(p, f"out[{i}]") for i, p in enumerate(out)])
+    check(lib().dit_ulysses_unpack_rope(ctypes.byref(layout), rank, _dev(recv, "recv"), arr,
+                                        _dev(rope_cos, "rope_cos"), _dev(rope_sin, "rope_sin"),
+                                        _stream(stream)), "dit_ulysses_unpack_rope")
     return out
 
 

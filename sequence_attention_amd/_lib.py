@@ -33,6 +33,7 @@ EXPORTS = (
     "dit_a2a_layout_init",
     "dit_ulysses_pack",
     "dit_ulysses_unpack",
+    "dit_ulysses_unpack_rope",
     "dit_attn_fwd",
     "dit_attn_merge",
     "dit_attn_fwd_merge",
@@ -85,6 +86,9 @@ def _declare(lib):
     lib.dit_ulysses_unpack.restype = ctypes.c_int
     lib.dit_ulysses_unpack.argtypes = [ctypes.POINTER(DitA2ALayout), ctypes.c_int, _I32, _P,
                                        ctypes.POINTER(_P), _P]
+    lib.dit_ulysses_unpack_rope.restype = ctypes.c_int
+    lib.dit_ulysses_unpack_rope.argtypes = [ctypes.POINTER(DitA2ALayout), _I32, _P, ctypes.POINTER(_P),
+                                            _P, _P, _P]
     lib.dit_attn_fwd.restype = ctypes.c_int
     lib.dit_attn_fwd.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                      ctypes.c_int, _P]

@@ -213,6 +213,56 @@ dit_status_t dit_ulysses_unpack(const dit_a2a_layout* layout, dit_a2a_dir_t dir,
   return run_permute(layout, (int)dir, rank, false, nullptr, recv_buf, out_planes, nullptr, stream);
 }
 
+dit_status_t dit_ulysses_unpack_rope(const dit_a2a_layout* L, int32_t rank, const void* recv_buf,
+                                     void* const* out_planes, const float* rope_cos,
+                                     const float* rope_sin, void* stream) {
+  dit_status_t st = check_permute(L, DIT_SEQ_TO_HEAD, rank);
+  if (st != DIT_OK) return st;
+  if (L->n_planes != 3)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "RoPE receive preparation takes the packed Q, K, V buffer "
+                                          "(n_planes = 3, got %d)", L->n_planes);
+  const int eb = dtype_bytes(L->dtype);
+  if (L->D % 2 != 0 || (L->D * eb) % 16 != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "head of %d x %d bytes is not a whole number of 16-byte vectors",
+                L->D, eb);
+  const int64_t buf_elems = L->elems_per_peer * L->U;
+  const int64_t plane_elems = (int64_t)L->B * L->S * L->H_loc * L->D;
+  if (buf_elems == 0 && plane_elems == 0) {
+    clear_error();
+    return DIT_OK;
+  }
+  if (out_planes == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "out_planes array is NULL");
+  if (recv_buf == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "recv_buf is NULL");
+  if (rope_cos == nullptr || rope_sin == nullptr)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "RoPE tables are NULL");
+  const size_t table_bytes = (size_t)L->S * (L->D / 2) * sizeof(float);
+  if (!aligned(recv_buf, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16))
+    return fail(DIT_ERR_UNSUPPORTED, "recv_buf and the RoPE tables must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if (out_planes[i] == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "out_planes[%d] is NULL", i);
+    if (!aligned(out_planes[i], 16))
+      return fail(DIT_ERR_UNSUPPORTED, "out_planes[%d] must be 16-byte aligned", i);
+    const size_t pb = (size_t)plane_elems * eb;
+    if (overlap(out_planes[i], pb, recv_buf, (size_t)buf_elems * eb) ||
+        overlap(out_planes[i], pb, rope_cos, table_bytes) || overlap(out_planes[i], pb, rope_sin, table_bytes))
+      return fail(DIT_ERR_INVALID_ARGUMENT, "out_planes[%d] overlaps an input", i);
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(out_planes[i], pb, out_planes[j], pb))
+        return fail(DIT_ERR_INVALID_ARGUMENT, "output planes %d and %d overlap", i, j);
+  }
+  dit::RopeUnpackArgs a;
+  a.recv = recv_buf;
+  for (int i = 0; i < 3; ++i) a.out[i] = out_planes[i];
+  a.cos = rope_cos;
+  a.sin = rope_sin;
+  a.B = L->B; a.S = L->S; a.D = L->D; a.U = L->U; a.n_planes = 3; a.S_loc = L->S_loc; a.H_loc = L->H_loc;
+  a.elem_bytes = eb;
+  a.is_f16 = (L->dtype == DIT_F16);
+  st = hip_status(dit::launch_rope_unpack(a, (hipStream_t)stream), "RoPE unpack launch");
+  if (st == DIT_OK) clear_error();
+  return st;
+}
+
 namespace {
 
 // dit_attn_fwd and dit_attn_fwd_merge: one validation path; `merge` makes

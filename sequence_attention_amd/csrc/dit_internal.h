@@ -63,6 +63,19 @@ struct PermuteArgs {
 
 hipError_t launch_permute(PermuteKind kind, const PermuteArgs& a, hipStream_t stream);
 
+// Sequence-to-head unpack with RoPE on planes 0 and 1 (Q, K); plane 2 copied.
+struct RopeUnpackArgs {
+  const void* recv;    // [U, n_planes, B, S_loc, H_loc, D]
+  void* out[3];        // n_planes x [B, S, H_loc, D]
+  const float* cos;    // [S, D/2]
+  const float* sin;    // [S, D/2]
+  int32_t B, S, D, U, n_planes, S_loc, H_loc;
+  int32_t elem_bytes;  // 2 (bf16 / f16) or 4 (f32); D * elem_bytes a multiple of 16
+  bool is_f16;
+};
+
+hipError_t launch_rope_unpack(const RopeUnpackArgs& a, hipStream_t stream);
+
 // ---- CFG combine ------------------------------------------------------------
 hipError_t launch_cfg_combine_f32(const float* u, const float* c, float* out, int64_t n, float g,
                                   hipStream_t stream);

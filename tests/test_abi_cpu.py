@@ -130,6 +130,32 @@ def test_pack_unpack_rejects(lib):
     assert pack(ctypes.byref(huge), 0, 0, ok3, send, NULL) == UNS
 
 
+def test_unpack_rope_rejects(lib):
+    # B=1, S=8, H=4, D=16 bf16, U=2: planes of 1*8*2*16 elements = 512 B
+    L3 = _layout(lib, 1, 8, 4, 16, 2, 1, 3, 0)
+    L1 = _layout(lib, 1, 8, 4, 16, 2, 1, 1, 0)
+    ok3 = _planes(A, A + 4096, A + 8192)
+    recv, cs, sn = P(A + 65536), P(A + 131072), P(A + 196608)
+    f = lib.dit_ulysses_unpack_rope
+    assert f(None, 0, recv, ok3, cs, sn, NULL) == INV
+    assert f(ctypes.byref(L1), 0, recv, ok3, cs, sn, NULL) == INV        # n_planes must be 3
+    assert f(ctypes.byref(L3), 2, recv, ok3, cs, sn, NULL) == INV        # rank
+    assert f(ctypes.byref(L3), 0, NULL, ok3, cs, sn, NULL) == INV        # recv
+    assert f(ctypes.byref(L3), 0, recv, None, cs, sn, NULL) == INV       # plane array
+    assert f(ctypes.byref(L3), 0, recv, ok3, NULL, sn, NULL) == INV      # tables
+    assert f(ctypes.byref(L3), 0, recv, ok3, cs, NULL, NULL) == INV
+    assert f(ctypes.byref(L3), 0, recv, _planes(A, 0, A + 8192), cs, sn, NULL) == INV
+    assert f(ctypes.byref(L3), 0, recv, _planes(A + 2, A + 4096, A + 8192), cs, sn, NULL) == UNS
+    assert f(ctypes.byref(L3), 0, recv, ok3, P(A + 131072 + 4), sn, NULL) == UNS
+    assert f(ctypes.byref(L3), 0, recv, _planes(A, A + 256, A + 8192), cs, sn, NULL) == INV  # overlap
+    assert f(ctypes.byref(L3), 0, P(A + 4096), ok3, cs, sn, NULL) == INV  # plane overlaps recv
+    assert f(ctypes.byref(L3), 0, recv, ok3, P(A + 8192), sn, NULL) == INV  # plane overlaps a table
+    L_small_d = _layout(lib, 1, 8, 4, 4, 2, 1, 3, 0)                      # 8-byte heads
+    assert f(ctypes.byref(L_small_d), 0, recv, ok3, cs, sn, NULL) == UNS
+    empty = _layout(lib, 0, 8, 4, 16, 2, 1, 3, 0)
+    assert f(ctypes.byref(empty), 0, NULL, _planes(0, 0, 0), NULL, NULL, NULL) == 0
+
+
 def test_empty_exchange_is_a_no_op(lib):
     L = _layout(lib, 0, 8, 4, 8, 2, 1, 3, 0)
     assert lib.dit_ulysses_pack(ctypes.byref(L), 0, 0, _planes(0, 0, 0), NULL, NULL) == 0
