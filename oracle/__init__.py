@@ -37,6 +37,7 @@ Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 
 from .reference import (  # noqa: F401
     attention,
+    attention_kv_len,
     merge,
     ring_attention,
     ring_hop_order,

@@ -89,6 +89,31 @@ def attention(q, k, v, scale: float, rows=None, row_group: int = 1024):
 # Online-softmax merge of partial results (ring hops)
 # ---------------------------------------------------------------------------
 
+def attention_kv_len(q, k, v, scale: float, kv_len, rows=None):
+    """Attention of batch b over its first kv_len[b] keys only.
+
+    SGLang "Parallelism Overview": the masked / tail-padded text path of
+    joint text+image attention; xLLM "DiT Architecture and Capability
+    Matrix": a replacement kernel preserves the padding exclusion.  Keys
+    past the valid length do not take part (their scores count as -inf);
+    a batch with no valid key gives the merge identity (O = 0, LSE = -inf).
+    kv_len values are clamped to [0, Skv].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    nr = Sq if rows is None else len(rows)
+    o = np.zeros((B, nr, H, D))
+    lse = np.full((B, H, nr), NEG_INF)
+    for b in range(B):
+        n = int(min(max(int(kv_len[b]), 0), Skv))
+        if n == 0:
+            continue
+        ob, lb = attention(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n], scale, rows=rows)
+        o[b], lse[b] = ob[0], lb[0]
+    return o, lse
+
+
 def merge(o_a, lse_a, o_c, lse_c):
     """Combine two partial attention results over disjoint key sets.
 

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from oracle import attention, brute
 
 RNG = np.random.default_rng(1234)
@@ -176,3 +177,41 @@ def test_a_planted_mistake_is_caught():
     _, lse_wrong = attention(q, k, v, 0.5)
     assert lse_right[0, 0, 0] == pytest.approx(math.log(6.0), abs=1e-14)
     assert abs(lse_wrong[0, 0, 0] - math.log(6.0)) > 0.1
+
+
+# ---- per-batch key lengths (tail-padded keys excluded) ------------------------
+
+def test_kv_len_matches_masked_scores_formulation():
+    # the slicing definition against an explicit -inf score mask followed by a
+    # softmax over all Skv keys (an independent formulation of the exclusion)
+    rng = np.random.default_rng(31)
+    B, Sq, Skv, H, D = 3, 5, 9, 2, 4
+    q, k, v = (rng.standard_normal(s) for s in ((B, Sq, H, D), (B, Skv, H, D), (B, Skv, H, D)))
+    kv_len = [9, 4, 1]
+    o, lse = oracle.attention_kv_len(q, k, v, 0.7, kv_len)
+    for b in range(B):
+        for h in range(H):
+            s = 0.7 * q[b, :, h] @ k[b, :, h].T
+            s[:, kv_len[b]:] = -np.inf
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            ref_o = (p / p.sum(axis=1, keepdims=True)) @ v[b, :, h]
+            ref_l = np.log(np.exp(s).sum(axis=1))
+            assert np.max(np.abs(o[b, :, h] - ref_o)) <= 1e-12
+            assert np.max(np.abs(lse[b, h] - ref_l)) <= 1e-12
+
+
+def test_kv_len_full_empty_and_chunking():
+    rng = np.random.default_rng(32)
+    B, Sq, Skv, H, D = 2, 4, 12, 2, 8
+    q, k, v = (rng.standard_normal(s) for s in ((B, Sq, H, D), (B, Skv, H, D), (B, Skv, H, D)))
+    full = oracle.attention(q, k, v, 0.3)
+    o, lse = oracle.attention_kv_len(q, k, v, 0.3, [Skv, 99])   # at and past Skv: all keys
+    assert np.max(np.abs(o - full[0])) <= 1e-13 and np.max(np.abs(lse - full[1])) <= 1e-13
+    o, lse = oracle.attention_kv_len(q, k, v, 0.3, [0, -3])     # no valid key: merge identity
+    assert not np.any(o) and np.all(np.isneginf(lse))
+    # a valid prefix split in two and merged equals the prefix at once
+    o7, l7 = oracle.attention_kv_len(q, k, v, 0.3, [7, 7])
+    a = oracle.attention(q, k[:, :3], v[:, :3], 0.3)
+    c = oracle.attention(q, k[:, 3:7], v[:, 3:7], 0.3)
+    m = oracle.merge(a[0], a[1], c[0], c[1])
+    assert np.max(np.abs(m[0] - o7)) <= 1e-13 and np.max(np.abs(m[1] - l7)) <= 1e-13
