@@ -292,6 +292,25 @@ def attention_configs(torch, sa, workloads, reps=10):
         "chunks": rw.R, "flop": fl, "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
         "frac_mfma_peak": round(fl / us / 1e6 / PEAK_BF16_TFLOPS, 4),
         "note": "hop 0 with dit_attn_fwd, hops 1-3 with dit_attn_fwd_merge (merge in the epilogue)"}
+    # joint text+image ring: the 4 image chunks as above, then a replicated,
+    # tail-padded text segment (512 slots, 300 valid) attended once with its
+    # valid length and merged into the same accumulator
+    k_txt = dev_randn((rw.B, 512, rw.H, rw.D), 7)
+    v_txt = dev_randn((rw.B, 512, rw.H, rw.D), 8)
+    txt_len = torch.full((rw.B,), 300, dtype=torch.int32, device="cuda")
+
+    def ring_joint(i):
+        ring_fused(i)
+        sa.dit_attn_fwd_kvlen(q, k_txt, v_txt, txt_len, o=o_acc, lse=lse_acc, scale=rw.scale, merge=True)
+
+    us = _time_launches(torch, ring_joint, reps)
+    fl_joint = 4 * rw.B * rw.H * rw.Sq * (rw.Skv + 300) * rw.D
+    res["attn_joint_text_image_ring_e2e"] = {
+        "flop": fl_joint, "us": round(us, 2), "TFLOP/s": round(fl_joint / us / 1e6, 1),
+        "frac_mfma_peak": round(fl_joint / us / 1e6 / PEAK_BF16_TFLOPS, 4),
+        "note": "ring of 4 image chunks (fused hops) + 300 valid of 512 text keys merged once; "
+                "FLOP counts valid keys only"}
+    del k_txt, v_txt
     kc, vc = k[:, :chunk], v[:, :chunk]
     us = _time_launches(torch, lambda i: sa.dit_attn_fwd(q, kc, vc, o=o_part, lse=lse_part, scale=rw.scale),
                         reps)

@@ -9,6 +9,7 @@
  *   dit_ulysses_unpack_rope                the receive-side unpack fused with
  *                                          RoPE on Q and K
  *   dit_attn_fwd                           attention with per-row LSE
+ *   dit_attn_fwd_kvlen                     ... over a per-batch key prefix
  *   dit_attn_merge                         online-softmax merge of partial
  *                                          results (ring hops)
  *   dit_attn_fwd_merge                     one ring hop: attention of a K/V
@@ -223,6 +224,30 @@ dit_status_t dit_ulysses_unpack_rope(const dit_a2a_layout* layout, int32_t rank,
 dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                           int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
                           dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* stream);
+
+/*
+ * Attention over a per-batch prefix of the keys: keys j >= kv_len[b] of
+ * batch b are excluded (their scores count as -inf), e.g. the tail padding
+ * of a fixed-length text segment (SGLang "Parallelism Overview": the
+ * masked / tail-padded text path of joint text+image attention; xLLM
+ * "DiT Architecture and Capability Matrix": a replacement kernel must keep
+ * the padding exclusion).  With merge = 1 the result is merged into
+ * (o, lse) as dit_attn_fwd_merge does, which is how a replicated text
+ * segment attended once is combined with the ring result.
+ *
+ * kv_len: [B] int32 DEVICE array, 4-byte aligned; values are clamped to
+ *   [0, Skv].  A batch with no valid key yields O = 0, LSE = -inf (merge = 0)
+ *   or leaves the accumulator unchanged (merge = 1).
+ * Other arguments as dit_attn_fwd (merge = 0) or dit_attn_fwd_merge
+ *   (merge = 1: o / lse are the accumulator, lse required).
+ * Tiles are never split into key chunks on this path (no workspace use).
+ * Errors: as dit_attn_fwd; INVALID_ARGUMENT also for a NULL kv_len or
+ * merge outside {0, 1}.
+ */
+dit_status_t dit_attn_fwd_kvlen(const void* q, const void* k, const void* v, const int32_t* kv_len,
+                                void* o, float* lse, int32_t B, int32_t Sq, int32_t Skv, int32_t H,
+                                int32_t D, float scale, dit_dtype_t in_dtype, dit_dtype_t o_dtype,
+                                int32_t merge, void* stream);
 
 /*
  * In-place online-softmax merge of a partial result into an accumulator

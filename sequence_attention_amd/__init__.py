@@ -28,7 +28,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "dit_abi_version", "dit_a2a_layout_init", "dit_ulysses_pack", "dit_ulysses_unpack",
     "dit_ulysses_unpack_rope",
-    "dit_attn_fwd", "dit_attn_merge", "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
+    "dit_attn_fwd", "dit_attn_fwd_kvlen", "dit_attn_merge", "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
 
@@ -164,6 +164,33 @@ def dit_attn_fwd(q, k, v, o=None, lse=None, scale=None, o_dtype=None, want_lse=T
     check(lib().dit_attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lse_ptr,
                              B, Sq, Skv, H, D, float(scale), in_code, _dtype_code(o.dtype),
                              _stream(stream)), "dit_attn_fwd")
+    return o, lse
+
+
+def dit_attn_fwd_kvlen(q, k, v, kv_len, o=None, lse=None, scale=None, o_dtype=None, merge=False,
+                       stream=None):
+    """Attention where batch b attends only to its first kv_len[b] keys
+    (kv_len: int32 GPU tensor [B]).  merge=True folds the result into the
+    accumulator (o, lse) instead of writing it."""
+    torch = _torch()
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if tuple(k.shape) != (B, Skv, H, D) or tuple(v.shape) != (B, Skv, H, D):
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,):
+        raise ValueError("kv_len must be an int32 tensor of shape [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if merge and (o is None or lse is None):
+        raise ValueError("merge=True needs the accumulator (o, lse)")
+    if o is None:
+        o = torch.empty((B, Sq, H, D), dtype=o_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    check(lib().dit_attn_fwd_kvlen(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(kv_len, "kv_len"),
+                                   _dev(o, "o"), _dev(lse, "lse"), B, Sq, Skv, H, D, float(scale),
+                                   _dtype_code(q.dtype), _dtype_code(o.dtype), 1 if merge else 0,
+                                   _stream(stream)), "dit_attn_fwd_kvlen")
     return o, lse
 
 

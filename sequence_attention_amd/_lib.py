@@ -35,6 +35,7 @@ EXPORTS = (
     "dit_ulysses_unpack",
     "dit_ulysses_unpack_rope",
     "dit_attn_fwd",
+    "dit_attn_fwd_kvlen",
     "dit_attn_merge",
     "dit_attn_fwd_merge",
     "dit_cfg_combine",
@@ -92,6 +93,9 @@ def _declare(lib):
     lib.dit_attn_fwd.restype = ctypes.c_int
     lib.dit_attn_fwd.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                      ctypes.c_int, _P]
+    lib.dit_attn_fwd_kvlen.restype = ctypes.c_int
+    lib.dit_attn_fwd_kvlen.argtypes = [_P, _P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                               ctypes.c_int, _I32, _P]
     lib.dit_attn_merge.restype = ctypes.c_int
     lib.dit_attn_merge.argtypes = [_P, _P, _P, _P] + [_I32] * 4 + [ctypes.c_int, _P]
     lib.dit_attn_fwd_merge.restype = ctypes.c_int

@@ -73,6 +73,7 @@ struct Params {
   float* lse;
   float* part;    // partial-result slots, one per workgroup of the split round
   int32_t* cnt;   // arrival counters of the split tiles, zero between launches
+  const int32_t* kv_len;  // valid keys per batch ([B], device), or null: all Skv
   int32_t Sq, Skv, H;
   int32_t n_qtiles;
   int32_t nblocks;   // key blocks per tile
@@ -192,12 +193,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     const uint32_t piece = whole ? 0 : j % p.split;
     const uint32_t tile = whole ? j : p.n_whole + j / p.split;
     const int kb0 = whole ? 0 : (int)((uint64_t)piece * nblocks / p.split);
-    const int kb1 = whole ? nblocks : (int)((uint64_t)(piece + 1) * nblocks / p.split);
 
     const int qt = tile % p.n_qtiles;
     const int bh = tile / p.n_qtiles;
     const int h = bh % p.H;
     const int b = bh / p.H;
+    // keys of this batch that take part: with per-batch lengths (tail-padded
+    // text) the keys past kv_len[b] are excluded, i.e. their scores are -inf
+    const int skv = p.kv_len != nullptr ? min(max(p.kv_len[b], 0), p.Skv) : p.Skv;
+    const int kb1 = min(whole ? nblocks : (int)((uint64_t)(piece + 1) * nblocks / p.split),
+                        (skv + kBN - 1) / kBN);
     const uint16_t* kbase = p.k + (size_t)b * p.Skv * rs + (size_t)h * D;
     const uint16_t* vbase = p.v + (size_t)b * p.Skv * rs + (size_t)h * D;
 
@@ -220,12 +225,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       const uint16_t* vb_ptr = vbase + (size_t)j0 * rs;
       const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb_ptr, (short)0, 0x7fffffff, kBufferWord3);
       const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb_ptr, (short)0, 0x7fffffff, kBufferWord3);
-      const bool tail = j0 + kBN > p.Skv;
+      const bool tail = j0 + kBN > skv;
 #pragma unroll
       for (int u = 0; u < INSTR_W; ++u) {
         uint32_t off = ld_off[u];
         if (tail) {
-          const int r = min(ld_row[u], p.Skv - 1 - j0);
+          const int r = min(ld_row[u], skv - 1 - j0);
           off = (uint32_t)(((size_t)r * rs + ld_col[u]) * 2);
         }
         const int dst = (wave * INSTR_W + u) * 1024;
@@ -282,13 +287,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         }
       }
       // lane holds S^T[key = 32t + 8(r/4) + 4g + r%4][query l32]
-      if (j0 + kBN > p.Skv) {
+      if (j0 + kBN > skv) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = j0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key >= p.Skv) s[t][r] = -INFINITY;
+            if (key >= skv) s[t][r] = -INFINITY;
           }
       }
       float mx = s[0][0];
@@ -346,6 +351,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
           }
         }
     };
+    if (kb1 <= kb0) {
+      // no key of this batch takes part (only with per-batch lengths, which
+      // never split tiles): the merge identity O = 0, LSE = -inf, or an
+      // accumulator left as it is
+      if constexpr (!kMerge) {
+        if (q_row < p.Sq) {
+          const size_t orow = ((size_t)b * p.Sq + q_row) * rs + (size_t)h * D;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int d = dt * 32 + 8 * u + 4 * g;
+              if constexpr (kOutF32)
+                *reinterpret_cast<float4*>(static_cast<float*>(p.o) + orow + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+              else
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = make_uint2(0u, 0u);
+            }
+          if (p.lse != nullptr && g == 0) p.lse[((size_t)b * p.H + h) * p.Sq + q_row] = -INFINITY;
+        }
+      }
+      return;
+    }
     issue(kb0, k_s0, v_s0);
     if (kb0 + 1 < kb1) issue(kb0 + 1, k_s1, v_s1);
     if (kb0 + 2 < kb1) issue(kb0 + 2, k_s2, v_s2);
@@ -502,6 +529,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.v = static_cast<const uint16_t*>(a.v);
   p.o = a.o;
   p.lse = a.lse;
+  p.kv_len = a.kv_len;
   p.Sq = a.Sq;
   p.Skv = a.Skv;
   p.H = a.H;
@@ -531,6 +559,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   const uint64_t slots = (uint64_t)cus * occupancy[dev];
   const uint64_t last = n_tiles % slots;  // tiles of the last, partial round
   uint64_t split = last == 0 ? 1 : std::min<uint64_t>({kMaxSplit, slots / last, (uint64_t)p.nblocks});
+  if (a.kv_len != nullptr) split = 1;  // per-batch lengths: whole tiles only
   if (split < 2) split = 1;
   p.n_whole = (uint32_t)(split > 1 ? n_tiles - last : n_tiles);
   p.split = (uint32_t)split;

@@ -24,8 +24,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const float* __restr
                                                             const float* __restrict__ k,
                                                             const float* __restrict__ v,
                                                             float* __restrict__ o,
-                                                            float* __restrict__ lse, int32_t Sq,
-                                                            int32_t Skv, int32_t H, float scale) {
+                                                            float* __restrict__ lse,
+                                                            const int32_t* __restrict__ kv_len,
+                                                            int32_t Sq, int32_t Skv, int32_t H,
+                                                            float scale) {
   constexpr int DH = D / 2;
   __shared__ float ks[kKeys][D];
   __shared__ float vs[kKeys][D];
@@ -34,6 +36,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const float* __restr
   const int i = blockIdx.x * kRows + (threadIdx.x >> 1);
   const bool row_ok = i < Sq;
   const size_t row_stride = (size_t)H * D;  // elements between consecutive sequence rows
+  // keys of this batch that take part (tail-padded keys are excluded)
+  const int skv = kv_len != nullptr ? min(max(kv_len[b], 0), Skv) : Skv;
+  if (skv == 0) {  // the merge identity, or an untouched accumulator
+    if (!kMerge && row_ok) {
+      float* op = o + ((size_t)b * Sq + i) * row_stride + (size_t)h * D + half * (D / 2);
+      for (int d = 0; d < D / 2; ++d) op[d] = 0.0f;
+      if (lse && half == 0) lse[((size_t)b * H + h) * Sq + i] = -INFINITY;
+    }
+    return;
+  }
 
   float qr[DH], acc[DH];
   const float* qp = q + ((size_t)b * Sq + (row_ok ? i : 0)) * row_stride + (size_t)h * D + half * DH;
@@ -44,17 +56,17 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const float* __restr
   }
   float m = -INFINITY, l = 0.0f;
 
-  for (int j0 = 0; j0 < Skv; j0 += kKeys) {
+  for (int j0 = 0; j0 < skv; j0 += kKeys) {
     __syncthreads();
     for (int e = threadIdx.x; e < kKeys * D; e += kThreads) {
       const int jj = e / D, d = e % D;
       const int j = j0 + jj;
-      const size_t off = ((size_t)b * Skv + (j < Skv ? j : 0)) * row_stride + (size_t)h * D + d;
-      ks[jj][d] = j < Skv ? k[off] : 0.0f;
-      vs[jj][d] = j < Skv ? v[off] : 0.0f;
+      const size_t off = ((size_t)b * Skv + (j < skv ? j : 0)) * row_stride + (size_t)h * D + d;
+      ks[jj][d] = j < skv ? k[off] : 0.0f;
+      vs[jj][d] = j < skv ? v[off] : 0.0f;
     }
     __syncthreads();
-    const int nk = min(kKeys, Skv - j0);
+    const int nk = min(kKeys, skv - j0);
     float s[kKeys];
     float mt = -INFINITY;
 #pragma unroll
@@ -116,11 +128,11 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   if (a.merge)
     attn_f32_kernel<D, true><<<grid, kThreads, 0, stream>>>(
         static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-        static_cast<float*>(a.o), a.lse, a.Sq, a.Skv, a.H, a.scale);
+        static_cast<float*>(a.o), a.lse, a.kv_len, a.Sq, a.Skv, a.H, a.scale);
   else
     attn_f32_kernel<D, false><<<grid, kThreads, 0, stream>>>(
         static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-        static_cast<float*>(a.o), a.lse, a.Sq, a.Skv, a.H, a.scale);
+        static_cast<float*>(a.o), a.lse, a.kv_len, a.Sq, a.Skv, a.H, a.scale);
   return hipGetLastError();
 }
 

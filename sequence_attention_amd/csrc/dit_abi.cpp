@@ -269,7 +269,8 @@ namespace {
 // (o, lse) an accumulator that this call merges into.
 dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
                        int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale, dit_dtype_t in_dtype,
-                       dit_dtype_t o_dtype, void* stream, bool merge) {
+                       dit_dtype_t o_dtype, void* stream, bool merge, const int32_t* kv_len = nullptr,
+                       bool has_kv_len = false) {
   if (B < 0 || Sq < 0 || Skv < 0 || H < 0 || D < 0)
     return fail(DIT_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Skv=%d H=%d D=%d)", B, Sq, Skv,
                 H, D);
@@ -289,6 +290,8 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
   }
   if (q == nullptr || o == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "q or o is NULL");
   if (merge && lse == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "the merge needs the accumulator's LSE");
+  if (has_kv_len && kv_len == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "kv_len is NULL");
+  if (has_kv_len && !aligned(kv_len, 4)) return fail(DIT_ERR_UNSUPPORTED, "kv_len not 4-byte aligned");
   if (Skv > 0 && (k == nullptr || v == nullptr))
     return fail(DIT_ERR_INVALID_ARGUMENT, "k or v is NULL");
   if (!aligned(q, 16) || !aligned(o, 16) || (Skv > 0 && (!aligned(k, 16) || !aligned(v, 16))))
@@ -318,6 +321,7 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
   dit::AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.merge = merge;
+  a.kv_len = has_kv_len ? kv_len : nullptr;
   a.B = B; a.Sq = Sq; a.Skv = Skv; a.H = H; a.D = D;
   a.scale = scale;
   a.o_f32 = (o_dtype == DIT_F32);
@@ -336,6 +340,15 @@ dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, 
                           int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
                           dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* stream) {
   return attn_call(q, k, v, o, lse, B, Sq, Skv, H, D, scale, in_dtype, o_dtype, stream, false);
+}
+
+dit_status_t dit_attn_fwd_kvlen(const void* q, const void* k, const void* v, const int32_t* kv_len,
+                                void* o, float* lse, int32_t B, int32_t Sq, int32_t Skv, int32_t H,
+                                int32_t D, float scale, dit_dtype_t in_dtype, dit_dtype_t o_dtype,
+                                int32_t merge, void* stream) {
+  if (merge != 0 && merge != 1) return fail(DIT_ERR_INVALID_ARGUMENT, "merge must be 0 or 1");
+  return attn_call(q, k, v, o, lse, B, Sq, Skv, H, D, scale, in_dtype, o_dtype, stream, merge == 1,
+                   kv_len, true);
 }
 
 dit_status_t dit_attn_fwd_merge(const void* q, const void* k, const void* v, void* o_acc,

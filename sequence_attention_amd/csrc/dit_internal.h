@@ -98,6 +98,7 @@ struct AttnArgs {
   float scale;
   bool o_f32;  // bf16 input only: write O as fp32
   bool merge = false;  // o / lse hold a partial result to merge this call into
+  const int32_t* kv_len = nullptr;  // [B] valid keys per batch (device), or null
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);

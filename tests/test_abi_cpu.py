@@ -219,6 +219,25 @@ def test_attn_fwd_merge_empty_chunk_is_a_no_op(lib):
     assert lib.dit_last_error().decode() == ""
 
 
+def _attn_kvlen(lib, q=A, k=A + 2**24, v=A + 2**25, kvl=A + 2**28, o=A + 2**26, lse=A + 2**27, B=1,
+                Sq=128, Skv=128, H=2, D=64, scale=0.125, din=0, dout=0, merge=0):
+    return lib.dit_attn_fwd_kvlen(P(q), P(k), P(v), P(kvl), P(o), P(lse), B, Sq, Skv, H, D, scale, din,
+                                  dout, merge, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kvl=0), INV), (dict(kvl=A + 2**28 + 2), UNS), (dict(merge=2), INV), (dict(merge=-1), INV),
+    (dict(merge=1, lse=0), INV), (dict(B=-1), INV), (dict(D=96), UNS), (dict(o=A + 1024), INV),
+])
+def test_attn_kvlen_rejects(lib, kw, code):
+    assert _attn_kvlen(lib, **kw) == code, lib.dit_last_error()
+
+
+def test_attn_kvlen_empty_is_a_no_op(lib):
+    assert _attn_kvlen(lib, q=0, k=0, v=0, o=0, lse=0, kvl=A, Sq=0) == 0
+    assert _attn_kvlen(lib, k=0, v=0, Skv=0, merge=1) == 0   # merging an empty key set
+
+
 def _merge(lib, oa=A, la=A + 2**24, op=A + 2**25, lp=A + 2**26, B=1, Sq=16, H=2, D=64, dt=0):
     return lib.dit_attn_merge(P(oa), P(la), P(op), P(lp), B, Sq, H, D, dt, NULL)
 
