@@ -19,7 +19,8 @@ Sources (cited by page title and section):
 * xLLM, "DiT Architecture and Capability Matrix" -- sequence padding to a
   multiple of lcm(SP, 64) and padding exclusion ("MiniMax-H3 boundaries").
 * cache-dit, "Context Parallelism" -- head padding before / after the
-  all-to-all ("Any Head Num" under UAA).
+  all-to-all ("Any Head Num" under UAA); the padding-free splits of
+  arbitrary sequence lengths and head counts (Ulysses Anything Attention).
 * The receive preparation with RoPE on Q and K (edge-dit.cpp "Parallel
   execution", Ulysses section) -- the RoPE convention is not on the pages;
   the RoFormer rotation of adjacent dims with caller-given cos / sin tables
@@ -49,6 +50,12 @@ from .reference import (  # noqa: F401
     pack_head_to_seq,
     unpack_head_to_seq,
     all_to_all,
+    pack_seq_to_head_uneven,
+    unpack_seq_to_head_uneven,
+    pack_head_to_seq_uneven,
+    unpack_head_to_seq_uneven,
+    uneven_chunk_sizes,
+    all_to_all_uneven,
     cfg_combine,
     cfg_combine_f32,
     fmaf,

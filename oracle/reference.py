@@ -334,6 +334,96 @@ def unpack_head_to_seq(recv, L, rank):
     return [out[i] for i in range(n)]
 
 
+# -- padding-free (uneven) splits ------------------------------------------------
+#
+# cache-dit "Context Parallelism" (Ulysses Anything Attention): arbitrary
+# sequence lengths without padding, each rank's length gathered from the
+# others; arbitrary head counts without padding (the no-pad variant).
+# Reading: rank r holds the contiguous rows [so[r], so[r] + S_r) of the
+# sequence and, inside attention, the contiguous heads [ho[r], ho[r] + H_r),
+# with so / ho the prefix sums of the per-rank counts.  The exchange buffer
+# is the concatenation, in peer order, of one chunk per peer (an all-to-all
+# with per-peer split sizes); each chunk is [n_planes, B, rows, heads, D].
+
+
+def _prefix(counts):
+    return np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))])
+
+
+def pack_seq_to_head_uneven(in_planes, seq_counts, head_counts, rank):
+    """Send buffer (1-D) of rank ``rank``: chunk p = in_pl[:, :, ho[p]:ho[p]+H_p]
+    for every plane; in_planes: n arrays [B, S_rank, H, D]."""
+    ho = _prefix(head_counts)
+    x = np.stack([np.asarray(t) for t in in_planes])          # [n, B, S_r, H, D]
+    assert x.shape[2] == seq_counts[rank] and x.shape[3] == ho[-1]
+    chunks = [x[:, :, :, ho[p]:ho[p + 1]].reshape(-1) for p in range(len(head_counts))]
+    return np.concatenate(chunks) if chunks else np.zeros(0, x.dtype)
+
+
+def unpack_seq_to_head_uneven(recv, B, D, n_planes, seq_counts, head_counts, rank):
+    """Planes [B, S, H_rank, D] from the receive buffer: the chunk from source
+    p holds rows [so[p], so[p] + S_p) of this rank's heads."""
+    H_r = head_counts[rank]
+    parts, off = [], 0
+    for p, S_p in enumerate(seq_counts):
+        size = n_planes * B * S_p * H_r * D
+        parts.append(np.asarray(recv)[off:off + size].reshape(n_planes, B, S_p, H_r, D))
+        off += size
+    assert off == np.asarray(recv).size
+    x = np.concatenate(parts, axis=2)                          # [n, B, S, H_r, D]
+    return [x[i] for i in range(n_planes)]
+
+
+def pack_head_to_seq_uneven(in_planes, seq_counts, head_counts, rank):
+    """Send buffer (1-D) of rank ``rank``: chunk p = rows [so[p], so[p] + S_p)
+    of every plane; in_planes: n arrays [B, S, H_rank, D]."""
+    so = _prefix(seq_counts)
+    x = np.stack([np.asarray(t) for t in in_planes])          # [n, B, S, H_r, D]
+    assert x.shape[2] == so[-1] and x.shape[3] == head_counts[rank]
+    chunks = [x[:, :, so[p]:so[p + 1]].reshape(-1) for p in range(len(seq_counts))]
+    return np.concatenate(chunks) if chunks else np.zeros(0, x.dtype)
+
+
+def unpack_head_to_seq_uneven(recv, B, D, n_planes, seq_counts, head_counts, rank):
+    """Planes [B, S_rank, H, D] from the receive buffer: the chunk from source
+    p holds heads [ho[p], ho[p] + H_p) of this rank's rows."""
+    S_r = seq_counts[rank]
+    parts, off = [], 0
+    for p, H_p in enumerate(head_counts):
+        size = n_planes * B * S_r * H_p * D
+        parts.append(np.asarray(recv)[off:off + size].reshape(n_planes, B, S_r, H_p, D))
+        off += size
+    assert off == np.asarray(recv).size
+    x = np.concatenate(parts, axis=3)                          # [n, B, S_r, H, D]
+    return [x[i] for i in range(n_planes)]
+
+
+def uneven_chunk_sizes(B, D, n_planes, seq_counts, head_counts, rank, seq_to_head=True):
+    """Elements rank ``rank`` sends to / receives from each peer."""
+    U = len(seq_counts)
+    if seq_to_head:
+        send = [n_planes * B * seq_counts[rank] * head_counts[p] * D for p in range(U)]
+        recv = [n_planes * B * seq_counts[p] * head_counts[rank] * D for p in range(U)]
+    else:
+        send = [n_planes * B * seq_counts[p] * head_counts[rank] * D for p in range(U)]
+        recv = [n_planes * B * seq_counts[rank] * head_counts[p] * D for p in range(U)]
+    return send, recv
+
+
+def all_to_all_uneven(sends, send_sizes):
+    """The exchange with per-peer split sizes (a test helper):
+    recv_r = concat over p of the part of send_p addressed to r."""
+    U = len(sends)
+    out = []
+    for r in range(U):
+        parts = []
+        for p in range(U):
+            off = int(sum(send_sizes[p][:r]))
+            parts.append(np.asarray(sends[p])[off:off + send_sizes[p][r]])
+        out.append(np.concatenate(parts))
+    return out
+
+
 def all_to_all(sends):
     """The exchange itself (a test helper; the library never performs it).
 
