@@ -21,6 +21,8 @@ Sources (cited by page title and section):
 * cache-dit, "Context Parallelism" -- head padding before / after the
   all-to-all ("Any Head Num" under UAA); the padding-free splits of
   arbitrary sequence lengths and head counts (Ulysses Anything Attention).
+* diffusers, "Distributed inference" (Ring Anything Attention) -- local K/V
+  padded to the longest rank, gathered, then cut back to the real lengths.
 * The receive preparation with RoPE on Q and K (edge-dit.cpp "Parallel
   execution", Ulysses section) -- the RoPE convention is not on the pages;
   the RoFormer rotation of adjacent dims with caller-given cos / sin tables
@@ -56,6 +58,8 @@ from .reference import (  # noqa: F401
     unpack_head_to_seq_uneven,
     uneven_chunk_sizes,
     all_to_all_uneven,
+    ring_anything_pad,
+    ring_anything_trim,
     cfg_combine,
     cfg_combine_f32,
     fmaf,

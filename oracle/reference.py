@@ -424,6 +424,34 @@ def all_to_all_uneven(sends, send_sizes):
     return out
 
 
+# -- Ring Anything: equal-size gather of uneven shards ----------------------------
+#
+# diffusers "Distributed inference" (Ring Anything Attention): each rank pads
+# its local K/V rows up to the largest rank's length, the padded buffers are
+# all-gathered, and the result is cut back to every rank's real length before
+# attention.  Reading: pad rows are zeros and sit after a rank's real rows
+# (per batch); the gathered buffer is rank-major [U, n, B, S_max, H, D].
+
+
+def ring_anything_pad(in_planes, S_max):
+    """[n, B, S_max, H, D] from n planes [B, S_r, H, D]; rows >= S_r are zero."""
+    x = np.stack([np.asarray(t) for t in in_planes])
+    n, B, S_r, H, D = x.shape
+    assert S_r <= S_max
+    out = np.zeros((n, B, S_max, H, D), dtype=x.dtype)
+    out[:, :, :S_r] = x
+    return out
+
+
+def ring_anything_trim(gathered, seq_counts):
+    """n planes [B, S, H, D] (S = sum of the counts) from the gathered buffer
+    [U, n, B, S_max, H, D]: rank p's first S_p rows, in rank order."""
+    g = np.asarray(gathered)
+    assert g.shape[0] == len(seq_counts) and max(seq_counts, default=0) <= g.shape[3]
+    x = np.concatenate([g[p, :, :, :seq_counts[p]] for p in range(len(seq_counts))], axis=2)
+    return [x[i] for i in range(x.shape[0])]
+
+
 def all_to_all(sends):
     """The exchange itself (a test helper; the library never performs it).
 

@@ -96,3 +96,31 @@ def test_chunk_sizes_balance():
     total_send = sum(sum(oracle.uneven_chunk_sizes(2, 4, 3, sc, hc, r, True)[0]) for r in range(3))
     total_recv = sum(sum(oracle.uneven_chunk_sizes(2, 4, 3, sc, hc, r, True)[1]) for r in range(3))
     assert total_send == total_recv == 3 * 2 * 12 * 6 * 4
+
+
+@pytest.mark.parametrize("counts,B,H,D,n", [([5, 3, 0, 4], 2, 3, 4, 2), ([7], 1, 2, 8, 1), ([2, 2], 3, 1, 2, 2)])
+def test_ring_anything_gather_recovers_the_sequence(counts, B, H, D, n):
+    S, S_max = sum(counts), max(counts)
+    rng = np.random.default_rng(S * 7 + n)
+    X = [rng.standard_normal((B, S, H, D)) for _ in range(n)]
+    so = np.concatenate([[0], np.cumsum(counts)])
+    padded = []
+    for r, c in enumerate(counts):
+        buf = oracle.ring_anything_pad([x[:, so[r]:so[r + 1]] for x in X], S_max)
+        assert buf.shape == (n, B, S_max, H, D)
+        assert not np.any(buf[:, :, c:])                        # pad rows are zeros
+        padded.append(buf)
+    gathered = np.stack(padded)                                 # the all-gather
+    out = oracle.ring_anything_trim(gathered, counts)
+    for a, b in zip(out, X):
+        assert np.array_equal(a, b)
+
+
+def test_ring_anything_trim_with_equal_counts_is_a_reshape():
+    rng = np.random.default_rng(3)
+    U, n, B, S_loc, H, D = 3, 2, 2, 4, 2, 3
+    g = rng.standard_normal((U, n, B, S_loc, H, D))
+    out = oracle.ring_anything_trim(g, [S_loc] * U)
+    want = np.transpose(g, (1, 2, 0, 3, 4, 5)).reshape(n, B, U * S_loc, H, D)
+    for i in range(n):
+        assert np.array_equal(out[i], want[i])
