@@ -194,6 +194,57 @@ def side_measurements(torch, sa, workloads, reps=20):
     res["flux_unpack_qkv_plain"] = {"bytes": moved, "us": round(us, 2), "GB/s": round(moved / us / 1e3, 1),
                                     "frac_hbm_peak": round(moved / us / 1e3 / PEAK_HBM_GBPS, 4)}
     del bufs
+    # padding-free split of FLUX at 1008x1008 (S = 512 text + 63*63 image = 4481
+    # rows over U = 4): packed QKV sequence-to-head pack and unpack of rank 0,
+    # against the padded layout of the same sequence; GB/s on the real bytes
+    S_u, U_u, H_u, D_u = 4481, 4, 24, 128
+    Lu = sa.dit_a2a_uneven_init(1, S_u, H_u, D_u, U_u, 3)
+    Lp = sa.dit_a2a_layout_init(1, S_u, H_u, D_u, U_u, 1, 3)
+    r_rows, _ = Lu.counts()
+    real = {"pack": 2 * 3 * r_rows[0] * H_u * D_u * 2,
+            "unpack": 2 * 3 * S_u * (H_u // U_u) * D_u * 2}
+    sets = max(2, math.ceil(2 * MALL_BYTES / (2 * real["pack"] + 2 * real["unpack"])) + 1)
+    bufs = []
+    for i in range(sets):
+        shard_u = [torch.empty((1, r_rows[0], H_u, D_u), dtype=torch.bfloat16, device="cuda").normal_()
+                   for _ in range(3)]
+        shard_p = [torch.empty((1, Lp.S_loc, H_u, D_u), dtype=torch.bfloat16, device="cuda").normal_()
+                   for _ in range(3)]
+        send_u = sa.dit_ulysses_pack_uneven(Lu, sa.DIT_SEQ_TO_HEAD, 0, shard_u)
+        send_p = sa.dit_ulysses_pack(Lp, sa.DIT_SEQ_TO_HEAD, 0, shard_p)
+        recv_u = torch.empty(sum(sa.dit_a2a_uneven_sizes(Lu, sa.DIT_SEQ_TO_HEAD, 0)[1]),
+                             dtype=torch.bfloat16, device="cuda").normal_()
+        out = [torch.empty((1, S_u, H_u // U_u, D_u), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+        bufs.append((shard_u, shard_p, send_u, send_p, recv_u, out))
+    legs = {
+        "flux1008_uneven_pack_qkv": ("pack", lambda b: sa.dit_ulysses_pack_uneven(
+            Lu, sa.DIT_SEQ_TO_HEAD, 0, b[0], send=b[2])),
+        "flux1008_padded_pack_qkv": ("pack", lambda b: sa.dit_ulysses_pack(
+            Lp, sa.DIT_SEQ_TO_HEAD, 0, b[1], send=b[3])),
+        "flux1008_uneven_unpack_qkv": ("unpack", lambda b: sa.dit_ulysses_unpack_uneven(
+            Lu, sa.DIT_SEQ_TO_HEAD, 0, b[4], out=b[5])),
+        "flux1008_padded_unpack_qkv": ("unpack", lambda b: sa.dit_ulysses_unpack(
+            Lp, sa.DIT_SEQ_TO_HEAD, 0, b[3], out=b[5])),
+    }
+    for name, (kind, fn) in legs.items():
+        us = _time_launches(torch, lambda i, fn=fn: fn(bufs[i % sets]), reps)
+        res[name] = {"real_bytes": real[kind], "us": round(us, 2), "GB/s": round(real[kind] / us / 1e3, 1),
+                     "frac_hbm_peak": round(real[kind] / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    del bufs
+    # Ring Anything trim of the gathered FLUX 1008x1008 K and V over a ring of 4
+    Lr = sa.dit_a2a_uneven_init(1, S_u, H_u, D_u, U_u, 1)
+    kv_bytes = S_u * H_u * D_u * 2
+    sets = max(2, math.ceil(2 * MALL_BYTES / (4 * kv_bytes)) + 1)
+    Lr2 = sa.dit_a2a_uneven_init(1, S_u, H_u, D_u, U_u, 2)
+    bufs = [(torch.empty((U_u, 2, 1, Lr.S_max, H_u, D_u), dtype=torch.bfloat16, device="cuda").normal_(),
+             [torch.empty((1, S_u, H_u, D_u), dtype=torch.bfloat16, device="cuda") for _ in range(2)])
+            for _ in range(sets)]
+    us = _time_launches(torch, lambda i: sa.dit_ring_anything_trim(Lr2, bufs[i % sets][0],
+                                                                  out=bufs[i % sets][1]), reps)
+    res["flux1008_ring_anything_trim_kv"] = {"real_bytes": 4 * kv_bytes, "us": round(us, 2),
+                                             "GB/s": round(4 * kv_bytes / us / 1e3, 1),
+                                             "frac_hbm_peak": round(4 * kv_bytes / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    del bufs
     # hipMemcpy-class device copy of the same bytes, as the achievable-copy reference
     n_bytes = 2 * 96_768_000 // 2
     src = [torch.empty(n_bytes // 2, dtype=torch.bfloat16, device="cuda") for _ in range(6)]

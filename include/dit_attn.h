@@ -8,6 +8,11 @@
  *                                          Ulysses all-to-alls
  *   dit_ulysses_unpack_rope                the receive-side unpack fused with
  *                                          RoPE on Q and K
+ *   dit_ulysses_pack_uneven / _unpack_uneven  the same transforms for
+ *                                          per-rank sequence and head counts
+ *                                          (no padding)
+ *   dit_ring_anything_pad / _trim          equal-size K/V gather of uneven
+ *                                          sequence shards
  *   dit_attn_fwd                           attention with per-row LSE
  *   dit_attn_fwd_kvlen                     ... over a per-batch key prefix
  *   dit_attn_merge                         online-softmax merge of partial
@@ -187,6 +192,112 @@ dit_status_t dit_ulysses_unpack(const dit_a2a_layout* layout, dit_a2a_dir_t dir,
 dit_status_t dit_ulysses_unpack_rope(const dit_a2a_layout* layout, int32_t rank, const void* recv_buf,
                                      void* const* out_planes, const float* rope_cos,
                                      const float* rope_sin, void* stream);
+
+/* Largest Ulysses (or ring) degree of the per-rank count layouts. */
+#define DIT_MAX_RANKS 64
+
+/*
+ * Layout of a padding-free Ulysses redistribution (cache-dit "Context
+ * Parallelism": Ulysses Anything Attention, any sequence length with zero
+ * padding after a scalar gather of every rank's length; the no-pad variant
+ * of Any Head Num).  Rank r holds the contiguous sequence rows
+ * [seq_offsets[r], seq_offsets[r] + seq_counts[r]) outside attention and the
+ * contiguous heads [head_offsets[r], head_offsets[r] + head_counts[r])
+ * inside it.  A count may be 0 (that rank then holds no rows / no heads).
+ * Unlike the padded layout nothing is zero-filled and nothing is dropped:
+ * every exchanged element is real.  Fill it with dit_a2a_uneven_init(); the
+ * derived fields (offsets, S_max) are read-only for callers.
+ *
+ * Exchange buffers are back-to-back chunks, one per peer in peer order (the
+ * split sizes of an all-to-all-v); each chunk is [n_planes, B, rows, heads,
+ * D].  dit_a2a_uneven_sizes() gives the element counts.
+ */
+typedef struct {
+  int32_t B, S, H, D, U;  /* S = sum of seq_counts, H = sum of head_counts */
+  int32_t n_planes;       /* 1 to 3 (3: packed Q, K, V; 2: K, V) */
+  dit_dtype_t dtype;
+  int32_t S_max;          /* derived: largest seq count */
+  int32_t seq_counts[DIT_MAX_RANKS];
+  int32_t head_counts[DIT_MAX_RANKS];
+  int32_t seq_offsets[DIT_MAX_RANKS + 1];  /* derived prefix sums */
+  int32_t head_offsets[DIT_MAX_RANKS + 1]; /* derived prefix sums */
+} dit_a2a_uneven_layout;
+
+/*
+ * Fill *out.  seq_counts / head_counts: HOST arrays of U non-negative counts
+ * summing to S / H, or NULL for the balanced split (count_r = floor(S/U),
+ * plus one on the first S mod U ranks; likewise for H).  B, S, H, D >= 0;
+ * 1 <= U <= DIT_MAX_RANKS; 1 <= n_planes <= 3.  Errors:
+ * DIT_ERR_INVALID_ARGUMENT (out NULL, negative size or count, counts not
+ * summing to S / H, bad U / n_planes / dtype, element counts overflowing
+ * int64).  Host-only.
+ */
+dit_status_t dit_a2a_uneven_init(int32_t B, int32_t S, int32_t H, int32_t D, int32_t U,
+                                 int32_t n_planes, dit_dtype_t dtype, const int32_t* seq_counts,
+                                 const int32_t* head_counts, dit_a2a_uneven_layout* out);
+
+/*
+ * Per-peer element counts of rank `rank`'s exchange in direction `dir`:
+ * send_counts[p] (chunk this rank sends to p) and recv_counts[p] (chunk it
+ * receives from p), HOST arrays of U entries (either may be NULL); chunk p
+ * of a buffer starts at the sum of the counts before it.
+ *   DIT_SEQ_TO_HEAD: send n*B*S_rank*H_p*D, receive n*B*S_p*H_rank*D.
+ *   DIT_HEAD_TO_SEQ: send n*B*S_p*H_rank*D, receive n*B*S_rank*H_p*D.
+ * Errors: INVALID_ARGUMENT (layout inconsistent with dit_a2a_uneven_init,
+ * bad direction or rank).  Host-only.
+ */
+dit_status_t dit_a2a_uneven_sizes(const dit_a2a_uneven_layout* layout, dit_a2a_dir_t dir,
+                                  int32_t rank, int64_t* send_counts, int64_t* recv_counts);
+
+/*
+ * Pack rank `rank`'s send buffer for a padding-free exchange.  With
+ * so / ho the seq / head offsets:
+ * DIT_SEQ_TO_HEAD: in_planes[pl] is the rank's shard [B, S_rank, H, D];
+ *   chunk p is [n, B, S_rank, H_p, D] = in_pl[:, :, ho[p] : ho[p] + H_p].
+ * DIT_HEAD_TO_SEQ: in_planes[pl] is the rank's head shard [B, S, H_rank, D];
+ *   chunk p is [n, B, S_p, H_rank, D] = in_pl[:, so[p] : so[p] + S_p].
+ * A bit copy; in_planes is a HOST array of n_planes device pointers; no
+ * aliasing between inputs and send_buf.  Errors: INVALID_ARGUMENT (layout,
+ * direction, rank, NULL pointer of a non-empty tensor, overlap);
+ * UNSUPPORTED (pointer not element-aligned, 2^31 or more elements on either
+ * side, B * n_planes above 65535); HIP.
+ */
+dit_status_t dit_ulysses_pack_uneven(const dit_a2a_uneven_layout* layout, dit_a2a_dir_t dir,
+                                     int32_t rank, const void* const* in_planes, void* send_buf,
+                                     void* stream);
+
+/*
+ * Unpack rank `rank`'s receive buffer (chunk p came from peer p):
+ * DIT_SEQ_TO_HEAD: out_planes[pl] is [B, S, H_rank, D]; rows
+ *   [so[p], so[p] + S_p) come from chunk p ([n, B, S_p, H_rank, D]).
+ * DIT_HEAD_TO_SEQ: out_planes[pl] is [B, S_rank, H, D]; heads
+ *   [ho[p], ho[p] + H_p) come from chunk p ([n, B, S_rank, H_p, D]).
+ * Every output element is written.  Errors as dit_ulysses_pack_uneven.
+ */
+dit_status_t dit_ulysses_unpack_uneven(const dit_a2a_uneven_layout* layout, dit_a2a_dir_t dir,
+                                       int32_t rank, const void* recv_buf, void* const* out_planes,
+                                       void* stream);
+
+/*
+ * Ring Anything (diffusers "Distributed inference", Ring Anything
+ * Attention): an all-gather needs equal sizes, so each ring rank pads its
+ * K/V shard to the longest rank's length, the padded shards are gathered,
+ * and the gathered buffer is cut back to the real lengths before attention.
+ * The layout's seq_counts are the ring ranks' lengths (head_counts unused:
+ * every rank keeps all H heads).
+ *
+ * dit_ring_anything_pad: in_planes[pl] is rank `rank`'s shard
+ *   [B, S_rank, H, D]; send_buf is [n, B, S_max, H, D] with rows >= S_rank
+ *   set to zero.
+ * dit_ring_anything_trim: gathered is [U, n, B, S_max, H, D] (rank-major);
+ *   out_planes[pl] is [B, S, H, D] with rows [so[p], so[p] + S_p) taken from
+ *   rank p's first S_p rows.  Pad rows are never read.
+ * Errors as dit_ulysses_pack_uneven.
+ */
+dit_status_t dit_ring_anything_pad(const dit_a2a_uneven_layout* layout, int32_t rank,
+                                   const void* const* in_planes, void* send_buf, void* stream);
+dit_status_t dit_ring_anything_trim(const dit_a2a_uneven_layout* layout, const void* gathered,
+                                    void* const* out_planes, void* stream);
 
 /*
  * Non-causal attention with per-row log-sum-exp (edge-dit.cpp "Parallel

@@ -22,12 +22,15 @@ import math
 from ._lib import (  # noqa: F401
     DIT_BF16, DIT_F16, DIT_F32, DIT_HEAD_TO_SEQ, DIT_OK, DIT_SEQ_TO_HEAD,
     DIT_ERR_HIP, DIT_ERR_INVALID_ARGUMENT, DIT_ERR_UNSUPPORTED,
-    DitA2ALayout, DitError, EXPORTS, LIB_PATH, check, lib,
+    DitA2ALayout, DitA2AUnevenLayout, DitError, EXPORTS, LIB_PATH, check, lib,
 )
 
 __all__ = [
     "dit_abi_version", "dit_a2a_layout_init", "dit_ulysses_pack", "dit_ulysses_unpack",
     "dit_ulysses_unpack_rope",
+    "dit_a2a_uneven_init", "dit_a2a_uneven_sizes", "dit_ulysses_pack_uneven",
+    "dit_ulysses_unpack_uneven", "dit_ring_anything_pad", "dit_ring_anything_trim",
+    "DitA2AUnevenLayout",
     "dit_attn_fwd", "dit_attn_fwd_kvlen", "dit_attn_merge", "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
@@ -139,6 +142,99 @@ def dit_ulysses_unpack_rope(layout: DitA2ALayout, rank: int, recv, rope_cos, rop
     check(lib().dit_ulysses_unpack_rope(ctypes.byref(layout), rank, _dev(recv, "recv"), arr,
                                         _dev(rope_cos, "rope_cos"), _dev(rope_sin, "rope_sin"),
                                         _stream(stream)), "dit_ulysses_unpack_rope")
+    return out
+
+
+def dit_a2a_uneven_init(B, S, H, D, U, n_planes=1, dtype=DIT_BF16, seq_counts=None,
+                        head_counts=None) -> DitA2AUnevenLayout:
+    """Padding-free layout from per-rank counts (None: the balanced split)."""
+    if not isinstance(dtype, int):
+        dtype = _dtype_code(dtype)
+
+    def arr(c):
+        if c is None:
+            return None
+        c = list(c)
+        if len(c) != U:
+            raise ValueError(f"expected {U} counts, got {len(c)}")
+        return (ctypes.c_int32 * U)(*c)
+
+    L = DitA2AUnevenLayout()
+    check(lib().dit_a2a_uneven_init(B, S, H, D, U, n_planes, dtype, arr(seq_counts), arr(head_counts),
+                                    ctypes.byref(L)), "dit_a2a_uneven_init")
+    return L
+
+
+def dit_a2a_uneven_sizes(layout: DitA2AUnevenLayout, direction: int, rank: int):
+    """(send_counts, recv_counts): elements exchanged with each peer."""
+    U = layout.U
+    send = (ctypes.c_int64 * U)()
+    recv = (ctypes.c_int64 * U)()
+    check(lib().dit_a2a_uneven_sizes(ctypes.byref(layout), direction, rank, send, recv),
+          "dit_a2a_uneven_sizes")
+    return list(send), list(recv)
+
+
+def _plane_ptrs(planes, name):
+    return (ctypes.c_void_p * 3)(*[_dev(p, f"{name}[{i}]") for i, p in enumerate(planes)])
+
+
+def dit_ulysses_pack_uneven(layout: DitA2AUnevenLayout, direction: int, rank: int, planes, send=None,
+                            stream=None):
+    """Pack rank `rank`'s planes into back-to-back per-peer chunks (1-D send
+    buffer, allocated if `send` is None)."""
+    torch = _torch()
+    planes = list(planes)
+    if len(planes) != layout.n_planes:
+        raise ValueError(f"expected {layout.n_planes} planes, got {len(planes)}")
+    if send is None:
+        n = sum(dit_a2a_uneven_sizes(layout, direction, rank)[0])
+        send = torch.empty(n, dtype=_torch_dtype(layout.dtype), device=planes[0].device)
+    check(lib().dit_ulysses_pack_uneven(ctypes.byref(layout), direction, rank, _plane_ptrs(planes, "planes"),
+                                        _dev(send, "send"), _stream(stream)), "dit_ulysses_pack_uneven")
+    return send
+
+
+def dit_ulysses_unpack_uneven(layout: DitA2AUnevenLayout, direction: int, rank: int, recv, out=None,
+                              stream=None):
+    """Unpack a receive buffer of per-peer chunks into n_planes tensors:
+    [B, S, H_rank, D] for DIT_SEQ_TO_HEAD, [B, S_rank, H, D] for DIT_HEAD_TO_SEQ."""
+    torch = _torch()
+    if out is None:
+        shape = ((layout.B, layout.S, layout.head_counts[rank], layout.D) if direction == DIT_SEQ_TO_HEAD
+                 else (layout.B, layout.seq_counts[rank], layout.H, layout.D))
+        out = [torch.empty(shape, dtype=_torch_dtype(layout.dtype), device=recv.device)
+               for _ in range(layout.n_planes)]
+    out = list(out)
+    check(lib().dit_ulysses_unpack_uneven(ctypes.byref(layout), direction, rank, _dev(recv, "recv"),
+                                          _plane_ptrs(out, "out"), _stream(stream)),
+          "dit_ulysses_unpack_uneven")
+    return out
+
+
+def dit_ring_anything_pad(layout: DitA2AUnevenLayout, rank: int, planes, send=None, stream=None):
+    """Rank `rank`'s shards [B, S_rank, H, D] padded into [n, B, S_max, H, D]."""
+    torch = _torch()
+    planes = list(planes)
+    if len(planes) != layout.n_planes:
+        raise ValueError(f"expected {layout.n_planes} planes, got {len(planes)}")
+    if send is None:
+        send = torch.empty((layout.n_planes, layout.B, layout.S_max, layout.H, layout.D),
+                           dtype=_torch_dtype(layout.dtype), device=planes[0].device)
+    check(lib().dit_ring_anything_pad(ctypes.byref(layout), rank, _plane_ptrs(planes, "planes"),
+                                      _dev(send, "send"), _stream(stream)), "dit_ring_anything_pad")
+    return send
+
+
+def dit_ring_anything_trim(layout: DitA2AUnevenLayout, gathered, out=None, stream=None):
+    """The gathered [U, n, B, S_max, H, D] buffer cut to n planes [B, S, H, D]."""
+    torch = _torch()
+    if out is None:
+        out = [torch.empty((layout.B, layout.S, layout.H, layout.D), dtype=_torch_dtype(layout.dtype),
+                           device=gathered.device) for _ in range(layout.n_planes)]
+    out = list(out)
+    check(lib().dit_ring_anything_trim(ctypes.byref(layout), _dev(gathered, "gathered"),
+                                       _plane_ptrs(out, "out"), _stream(stream)), "dit_ring_anything_trim")
     return out
 
 

@@ -34,6 +34,12 @@ EXPORTS = (
     "dit_ulysses_pack",
     "dit_ulysses_unpack",
     "dit_ulysses_unpack_rope",
+    "dit_a2a_uneven_init",
+    "dit_a2a_uneven_sizes",
+    "dit_ulysses_pack_uneven",
+    "dit_ulysses_unpack_uneven",
+    "dit_ring_anything_pad",
+    "dit_ring_anything_trim",
     "dit_attn_fwd",
     "dit_attn_fwd_kvlen",
     "dit_attn_merge",
@@ -57,6 +63,32 @@ class DitA2ALayout(ctypes.Structure):
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+DIT_MAX_RANKS = 64
+
+
+class DitA2AUnevenLayout(ctypes.Structure):
+    """Mirror of dit_a2a_uneven_layout."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("U", ctypes.c_int32),
+        ("n_planes", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+        ("S_max", ctypes.c_int32),
+        ("seq_counts", ctypes.c_int32 * DIT_MAX_RANKS),
+        ("head_counts", ctypes.c_int32 * DIT_MAX_RANKS),
+        ("seq_offsets", ctypes.c_int32 * (DIT_MAX_RANKS + 1)),
+        ("head_offsets", ctypes.c_int32 * (DIT_MAX_RANKS + 1)),
+    ]
+
+    def counts(self):
+        U = self.U
+        return list(self.seq_counts[:U]), list(self.head_counts[:U])
+
+    def offsets(self):
+        U = self.U
+        return list(self.seq_offsets[:U + 1]), list(self.head_offsets[:U + 1])
 
 
 class DitError(RuntimeError):
@@ -90,6 +122,21 @@ def _declare(lib):
     lib.dit_ulysses_unpack_rope.restype = ctypes.c_int
     lib.dit_ulysses_unpack_rope.argtypes = [ctypes.POINTER(DitA2ALayout), _I32, _P, ctypes.POINTER(_P),
                                             _P, _P, _P]
+    _UL = ctypes.POINTER(DitA2AUnevenLayout)
+    _I32P = ctypes.POINTER(_I32)
+    _I64P = ctypes.POINTER(ctypes.c_int64)
+    lib.dit_a2a_uneven_init.restype = ctypes.c_int
+    lib.dit_a2a_uneven_init.argtypes = [_I32] * 6 + [ctypes.c_int, _I32P, _I32P, _UL]
+    lib.dit_a2a_uneven_sizes.restype = ctypes.c_int
+    lib.dit_a2a_uneven_sizes.argtypes = [_UL, ctypes.c_int, _I32, _I64P, _I64P]
+    lib.dit_ulysses_pack_uneven.restype = ctypes.c_int
+    lib.dit_ulysses_pack_uneven.argtypes = [_UL, ctypes.c_int, _I32, ctypes.POINTER(_P), _P, _P]
+    lib.dit_ulysses_unpack_uneven.restype = ctypes.c_int
+    lib.dit_ulysses_unpack_uneven.argtypes = [_UL, ctypes.c_int, _I32, _P, ctypes.POINTER(_P), _P]
+    lib.dit_ring_anything_pad.restype = ctypes.c_int
+    lib.dit_ring_anything_pad.argtypes = [_UL, _I32, ctypes.POINTER(_P), _P, _P]
+    lib.dit_ring_anything_trim.restype = ctypes.c_int
+    lib.dit_ring_anything_trim.argtypes = [_UL, _P, ctypes.POINTER(_P), _P]
     lib.dit_attn_fwd.restype = ctypes.c_int
     lib.dit_attn_fwd.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                      ctypes.c_int, _P]

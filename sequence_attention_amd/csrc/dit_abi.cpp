@@ -265,6 +265,257 @@ dit_status_t dit_ulysses_unpack_rope(const dit_a2a_layout* L, int32_t rank, cons
 
 namespace {
 
+// ---- padding-free (uneven) layouts ---------------------------------------------
+
+void balanced_split(int32_t total, int32_t U, int32_t* counts) {
+  for (int r = 0; r < U; ++r) counts[r] = total / U + (r < total % U ? 1 : 0);
+}
+
+dit_status_t derive_uneven(int32_t B, int32_t S, int32_t H, int32_t D, int32_t U, int32_t n_planes,
+                           dit_dtype_t dtype, const int32_t* seq_counts, const int32_t* head_counts,
+                           dit_a2a_uneven_layout* L) {
+  if (B < 0 || S < 0 || H < 0 || D < 0)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "negative size (B=%d S=%d H=%d D=%d)", B, S, H, D);
+  if (U < 1 || U > DIT_MAX_RANKS)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "degree U=%d outside [1, %d]", U, DIT_MAX_RANKS);
+  if (n_planes < 1 || n_planes > 3)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "n_planes=%d outside [1, 3]", n_planes);
+  if (!dtype_ok(dtype)) return fail(DIT_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dtype);
+  memset(L, 0, sizeof(*L));
+  L->B = B; L->S = S; L->H = H; L->D = D; L->U = U; L->n_planes = n_planes; L->dtype = dtype;
+  if (seq_counts) memcpy(L->seq_counts, seq_counts, sizeof(int32_t) * U);
+  else balanced_split(S, U, L->seq_counts);
+  if (head_counts) memcpy(L->head_counts, head_counts, sizeof(int32_t) * U);
+  else balanced_split(H, U, L->head_counts);
+  int64_t so = 0, ho = 0;
+  for (int r = 0; r < U; ++r) {
+    if (L->seq_counts[r] < 0 || L->head_counts[r] < 0)
+      return fail(DIT_ERR_INVALID_ARGUMENT, "negative count for rank %d", r);
+    L->seq_offsets[r] = (int32_t)so;
+    L->head_offsets[r] = (int32_t)ho;
+    so += L->seq_counts[r];
+    ho += L->head_counts[r];
+    if (so > S || ho > H) break;
+    if (L->seq_counts[r] > L->S_max) L->S_max = L->seq_counts[r];
+  }
+  if (so != S || ho != H)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "counts sum to S=%lld H=%lld, expected S=%d H=%d",
+                (long long)so, (long long)ho, S, H);
+  L->seq_offsets[U] = S;
+  L->head_offsets[U] = H;
+  int64_t e = n_planes;
+  if (!mul_ok(e, B) || !mul_ok(e, S) || !mul_ok(e, H) || !mul_ok(e, D) ||
+      !mul_ok(e, U))  // covers the padded Ring Anything gather U*n*B*S_max*H*D as well
+    return fail(DIT_ERR_INVALID_ARGUMENT, "element count overflows int64");
+  return DIT_OK;
+}
+
+dit_status_t check_uneven(const dit_a2a_uneven_layout* L) {
+  if (L == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "layout is NULL");
+  if (L->U < 1 || L->U > DIT_MAX_RANKS)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "degree U=%d outside [1, %d]", L->U, DIT_MAX_RANKS);
+  dit_a2a_uneven_layout ref;
+  const dit_status_t st = derive_uneven(L->B, L->S, L->H, L->D, L->U, L->n_planes, L->dtype,
+                                        L->seq_counts, L->head_counts, &ref);
+  if (st != DIT_OK) return st;
+  if (ref.S_max != L->S_max ||
+      memcmp(ref.seq_offsets, L->seq_offsets, sizeof(int32_t) * (L->U + 1)) != 0 ||
+      memcmp(ref.head_offsets, L->head_offsets, sizeof(int32_t) * (L->U + 1)) != 0)
+    return fail(DIT_ERR_INVALID_ARGUMENT,
+                "layout derived fields do not match its counts (use dit_a2a_uneven_init)");
+  return DIT_OK;
+}
+
+// The chunk geometry of one padding-free map (see launch_chunk_copy), with
+// the element counts of both sides for validation.
+struct UnevenPlan {
+  dit::ChunkCopyArgs a;
+  int64_t plane_elems;  // one plane
+  int64_t buf_elems;    // the whole buffer
+};
+
+void plan_uneven(const dit_a2a_uneven_layout* L, int dir, int32_t r, bool pack, UnevenPlan* P) {
+  dit::ChunkCopyArgs& a = P->a;
+  memset(&a, 0, sizeof(a));
+  const int64_t n = L->n_planes, B = L->B, D = L->D;
+  a.to_chunk = pack;
+  a.n_planes = L->n_planes; a.B = L->B; a.D = L->D; a.elem_bytes = dtype_bytes(L->dtype);
+  a.n_peers = L->U;
+  // head-slice maps move head windows of rank r's own rows; row-block maps
+  // move row windows of rank r's own heads.
+  const bool head_slice = (dir == DIT_SEQ_TO_HEAD) == pack;
+  int64_t off = 0;
+  if (head_slice) {
+    const int64_t R = L->seq_counts[r];
+    a.plane_b_rows = R;
+    a.plane_row = (int64_t)L->H * D;
+    for (int p = 0; p < L->U; ++p) {
+      const int64_t Hp = L->head_counts[p];
+      a.peer[p] = {R, R, Hp * D, (int64_t)L->head_offsets[p] * D, off};
+      off += n * B * R * Hp * D;
+    }
+    P->plane_elems = B * R * L->H * D;
+  } else {
+    const int64_t Hr = L->head_counts[r];
+    a.plane_b_rows = L->S;
+    a.plane_row = Hr * D;
+    for (int p = 0; p < L->U; ++p) {
+      const int64_t Sp = L->seq_counts[p];
+      a.peer[p] = {Sp, Sp, Hr * D, (int64_t)L->seq_offsets[p] * Hr * D, off};
+      off += n * B * Sp * Hr * D;
+    }
+    P->plane_elems = B * (int64_t)L->S * Hr * D;
+  }
+  P->buf_elems = off;
+}
+
+void plan_ring_anything(const dit_a2a_uneven_layout* L, int32_t r, bool pad, UnevenPlan* P) {
+  dit::ChunkCopyArgs& a = P->a;
+  memset(&a, 0, sizeof(a));
+  const int64_t n = L->n_planes, B = L->B, HD = (int64_t)L->H * L->D, Smax = L->S_max;
+  a.to_chunk = pad;
+  a.n_planes = L->n_planes; a.B = L->B; a.D = L->D; a.elem_bytes = dtype_bytes(L->dtype);
+  a.plane_row = HD;
+  if (pad) {
+    a.n_peers = 1;
+    a.plane_b_rows = L->seq_counts[r];
+    a.peer[0] = {L->seq_counts[r], Smax, HD, 0, 0};
+    P->plane_elems = B * L->seq_counts[r] * HD;
+    P->buf_elems = n * B * Smax * HD;
+  } else {
+    a.n_peers = L->U;
+    a.plane_b_rows = L->S;
+    for (int p = 0; p < L->U; ++p)
+      a.peer[p] = {L->seq_counts[p], Smax, HD, (int64_t)L->seq_offsets[p] * HD, p * n * B * Smax * HD};
+    P->plane_elems = B * (int64_t)L->S * HD;
+    P->buf_elems = L->U * n * B * Smax * HD;
+  }
+}
+
+dit_status_t run_uneven(const dit_a2a_uneven_layout* L, UnevenPlan& P, const void* const* planes_in,
+                        const void* buf_in, void* const* planes_out, void* buf_out, void* stream) {
+  const bool pack = P.a.to_chunk;
+  const int eb = dtype_bytes(L->dtype);
+  if (P.buf_elems == 0 && P.plane_elems == 0) {
+    clear_error();
+    return DIT_OK;
+  }
+  if (P.buf_elems >= ((int64_t)1 << 31) || P.plane_elems >= ((int64_t)1 << 31))
+    return fail(DIT_ERR_UNSUPPORTED, "2^31 or more elements on one side of the copy");
+  if ((int64_t)L->n_planes * L->B > 65535)
+    return fail(DIT_ERR_UNSUPPORTED, "B * n_planes = %lld exceeds 65535",
+                (long long)L->n_planes * L->B);
+  const char* side = pack ? "in_planes" : "out_planes";
+  const void* const* planes = pack ? planes_in : (const void* const*)planes_out;
+  if (planes == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "%s array is NULL", side);
+  for (int i = 0; i < L->n_planes; ++i) {
+    if (P.plane_elems > 0 && planes[i] == nullptr)
+      return fail(DIT_ERR_INVALID_ARGUMENT, "%s[%d] is NULL", side, i);
+    if (!aligned(planes[i], eb))
+      return fail(DIT_ERR_UNSUPPORTED, "%s[%d] not aligned to its element size", side, i);
+  }
+  const void* buf = pack ? (const void*)buf_out : buf_in;
+  if (P.buf_elems > 0 && buf == nullptr)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "exchange buffer is NULL");
+  if (!aligned(buf, eb)) return fail(DIT_ERR_UNSUPPORTED, "exchange buffer not element-aligned");
+  const size_t pb = (size_t)P.plane_elems * eb;
+  for (int i = 0; i < L->n_planes; ++i) {
+    if (overlap(planes[i], pb, buf, (size_t)P.buf_elems * eb))
+      return fail(DIT_ERR_INVALID_ARGUMENT, "plane %d overlaps the exchange buffer", i);
+    if (!pack)
+      for (int j = i + 1; j < L->n_planes; ++j)
+        if (overlap(planes[i], pb, planes[j], pb))
+          return fail(DIT_ERR_INVALID_ARGUMENT, "output planes %d and %d overlap", i, j);
+  }
+  for (int i = 0; i < L->n_planes; ++i) P.a.planes[i] = const_cast<void*>(planes[i]);
+  P.a.chunk = const_cast<void*>(buf);
+  const dit_status_t st =
+      hip_status(dit::launch_chunk_copy(P.a, (hipStream_t)stream), "chunk copy launch");
+  if (st == DIT_OK) clear_error();
+  return st;
+}
+
+dit_status_t check_dir_rank(const dit_a2a_uneven_layout* L, int dir, int32_t rank) {
+  if (dir != DIT_SEQ_TO_HEAD && dir != DIT_HEAD_TO_SEQ)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "unknown direction %d", dir);
+  if (rank < 0 || rank >= L->U)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "rank %d outside [0, U=%d)", rank, L->U);
+  return DIT_OK;
+}
+
+}  // namespace
+
+dit_status_t dit_a2a_uneven_init(int32_t B, int32_t S, int32_t H, int32_t D, int32_t U,
+                                 int32_t n_planes, dit_dtype_t dtype, const int32_t* seq_counts,
+                                 const int32_t* head_counts, dit_a2a_uneven_layout* out) {
+  if (out == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "out is NULL");
+  dit_a2a_uneven_layout L;
+  const dit_status_t st = derive_uneven(B, S, H, D, U, n_planes, dtype, seq_counts, head_counts, &L);
+  if (st != DIT_OK) return st;
+  *out = L;
+  clear_error();
+  return DIT_OK;
+}
+
+dit_status_t dit_a2a_uneven_sizes(const dit_a2a_uneven_layout* L, dit_a2a_dir_t dir, int32_t rank,
+                                  int64_t* send_counts, int64_t* recv_counts) {
+  dit_status_t st = check_uneven(L);
+  if (st == DIT_OK) st = check_dir_rank(L, (int)dir, rank);
+  if (st != DIT_OK) return st;
+  const int64_t base = (int64_t)L->n_planes * L->B * L->D;
+  for (int p = 0; p < L->U; ++p) {
+    const int64_t mine_s = L->seq_counts[rank], mine_h = L->head_counts[rank];
+    const int64_t peer_s = L->seq_counts[p], peer_h = L->head_counts[p];
+    const int64_t out_e = dir == DIT_SEQ_TO_HEAD ? base * mine_s * peer_h : base * peer_s * mine_h;
+    const int64_t in_e = dir == DIT_SEQ_TO_HEAD ? base * peer_s * mine_h : base * mine_s * peer_h;
+    if (send_counts) send_counts[p] = out_e;
+    if (recv_counts) recv_counts[p] = in_e;
+  }
+  clear_error();
+  return DIT_OK;
+}
+
+dit_status_t dit_ulysses_pack_uneven(const dit_a2a_uneven_layout* L, dit_a2a_dir_t dir, int32_t rank,
+                                     const void* const* in_planes, void* send_buf, void* stream) {
+  dit_status_t st = check_uneven(L);
+  if (st == DIT_OK) st = check_dir_rank(L, (int)dir, rank);
+  if (st != DIT_OK) return st;
+  UnevenPlan P;
+  plan_uneven(L, (int)dir, rank, true, &P);
+  return run_uneven(L, P, in_planes, nullptr, nullptr, send_buf, stream);
+}
+
+dit_status_t dit_ulysses_unpack_uneven(const dit_a2a_uneven_layout* L, dit_a2a_dir_t dir, int32_t rank,
+                                       const void* recv_buf, void* const* out_planes, void* stream) {
+  dit_status_t st = check_uneven(L);
+  if (st == DIT_OK) st = check_dir_rank(L, (int)dir, rank);
+  if (st != DIT_OK) return st;
+  UnevenPlan P;
+  plan_uneven(L, (int)dir, rank, false, &P);
+  return run_uneven(L, P, nullptr, recv_buf, out_planes, nullptr, stream);
+}
+
+dit_status_t dit_ring_anything_pad(const dit_a2a_uneven_layout* L, int32_t rank,
+                                   const void* const* in_planes, void* send_buf, void* stream) {
+  dit_status_t st = check_uneven(L);
+  if (st == DIT_OK) st = check_dir_rank(L, DIT_SEQ_TO_HEAD, rank);
+  if (st != DIT_OK) return st;
+  UnevenPlan P;
+  plan_ring_anything(L, rank, true, &P);
+  return run_uneven(L, P, in_planes, nullptr, nullptr, send_buf, stream);
+}
+
+dit_status_t dit_ring_anything_trim(const dit_a2a_uneven_layout* L, const void* gathered,
+                                    void* const* out_planes, void* stream) {
+  const dit_status_t st = check_uneven(L);
+  if (st != DIT_OK) return st;
+  UnevenPlan P;
+  plan_ring_anything(L, 0, false, &P);
+  return run_uneven(L, P, nullptr, gathered, out_planes, nullptr, stream);
+}
+
+namespace {
+
 // dit_attn_fwd and dit_attn_fwd_merge: one validation path; `merge` makes
 // (o, lse) an accumulator that this call merges into.
 dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,

@@ -63,6 +63,31 @@ struct PermuteArgs {
 
 hipError_t launch_permute(PermuteKind kind, const PermuteArgs& a, hipStream_t stream);
 
+// Per-peer chunk copies between planes and a buffer of back-to-back chunks
+// of per-peer sizes (padding-free Ulysses maps, Ring Anything pad / trim).
+// For peer p and every plane pl, batch b, row s < chunk_rows, element e < run:
+//   buffer  [chunk_off + ((pl*B + b)*chunk_rows + s)*run + e]
+//   plane_pl[(b*plane_b_rows + s)*plane_row + plane_off + e]
+// are copied for s < rows (direction set by to_chunk); toward the buffer,
+// rows s >= rows are written as zeros.  Sizes and offsets are in elements;
+// run, plane_off, plane_row and chunk_off are multiples of D.
+constexpr int kMaxPeers = 64;
+
+struct ChunkPeer {
+  int64_t rows, chunk_rows, run, plane_off, chunk_off;
+};
+
+struct ChunkCopyArgs {
+  void* planes[3];
+  void* chunk;
+  bool to_chunk;
+  int32_t n_planes, B, D, elem_bytes, n_peers;
+  int64_t plane_b_rows, plane_row;
+  ChunkPeer peer[kMaxPeers];
+};
+
+hipError_t launch_chunk_copy(const ChunkCopyArgs& a, hipStream_t stream);
+
 // Sequence-to-head unpack with RoPE on planes 0 and 1 (Q, K); plane 2 copied.
 struct RopeUnpackArgs {
   const void* recv;    // [U, n_planes, B, S_loc, H_loc, D]

@@ -279,3 +279,100 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         sa.dit_attn_fwd(q, q, q, o=q.clone(), lse=torch.zeros(1, 1, 4))
+
+
+# ---- padding-free (uneven) layouts ---------------------------------------------
+
+def _uneven(lib, B, S, H, D, U, n=1, dt=0, sc=None, hc=None):
+    L = _lib.DitA2AUnevenLayout()
+    arr = lambda c: None if c is None else (ctypes.c_int32 * U)(*c)
+    st = lib.dit_a2a_uneven_init(B, S, H, D, U, n, dt, arr(sc), arr(hc), ctypes.byref(L))
+    assert st == 0, lib.dit_last_error()
+    return L
+
+
+@pytest.mark.parametrize("S,H,U,sc,hc", [
+    (4481, 24, 4, None, None), (10, 5, 3, None, None), (9, 5, 3, [0, 4, 5], [2, 0, 3]),
+    (7, 1, 4, None, None), (0, 0, 2, None, None),
+])
+def test_uneven_layout_and_sizes_match_oracle(lib, S, H, U, sc, hc):
+    B, D, n = 2, 8, 3
+    L = _uneven(lib, B, S, H, D, U, n, 0, sc, hc)
+    want_s = sc or [S // U + (1 if r < S % U else 0) for r in range(U)]
+    want_h = hc or [H // U + (1 if r < H % U else 0) for r in range(U)]
+    assert L.counts() == (want_s, want_h)
+    so, ho = L.offsets()
+    assert so == [sum(want_s[:r]) for r in range(U + 1)] and ho == [sum(want_h[:r]) for r in range(U + 1)]
+    assert L.S_max == max(want_s)
+    for r in range(U):
+        for d, s2h in ((0, True), (1, False)):
+            send = (ctypes.c_int64 * U)()
+            recv = (ctypes.c_int64 * U)()
+            assert lib.dit_a2a_uneven_sizes(ctypes.byref(L), d, r, send, recv) == 0
+            ws, wr = oracle.uneven_chunk_sizes(B, D, n, want_s, want_h, r, s2h)
+            assert list(send) == ws and list(recv) == wr
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 10, 4, 8, 0, 1, 0, None, None), INV),                 # U = 0
+    ((1, 10, 4, 8, 65, 1, 0, None, None), INV),                # U > DIT_MAX_RANKS
+    ((1, 10, 4, 8, 2, 4, 0, None, None), INV),                 # n_planes
+    ((1, 10, 4, 8, 2, 0, 0, None, None), INV),
+    ((1, 10, 4, 8, 2, 1, 9, None, None), INV),                 # dtype
+    ((-1, 10, 4, 8, 2, 1, 0, None, None), INV),
+    ((1, 10, 4, 8, 2, 1, 0, [5, 6], None), INV),               # counts sum to 11, not 10
+    ((1, 10, 4, 8, 2, 1, 0, None, [1, 2]), INV),               # heads sum to 3, not 4
+    ((1, 10, 4, 8, 2, 1, 0, [12, -2], None), INV),             # negative count
+])
+def test_uneven_init_rejects(lib, args, code):
+    B, S, H, D, U, n, dt, sc, hc = args
+    arr = lambda c: None if c is None else (ctypes.c_int32 * len(c))(*c)
+    L = _lib.DitA2AUnevenLayout()
+    assert lib.dit_a2a_uneven_init(B, S, H, D, U, n, dt, arr(sc), arr(hc), ctypes.byref(L)) == code
+    assert lib.dit_a2a_uneven_init(1, 10, 4, 8, 2, 1, 0, None, None, None) == INV
+
+
+def test_uneven_pack_unpack_rejects(lib):
+    L = _uneven(lib, 1, 9, 5, 8, 3, 3, 0, [4, 0, 5], [2, 2, 1])
+    ok3 = _planes(A, A + 4096, A + 8192)
+    buf = P(A + 65536)
+    pk, up = lib.dit_ulysses_pack_uneven, lib.dit_ulysses_unpack_uneven
+    assert pk(None, 0, 0, ok3, buf, NULL) == INV
+    assert pk(ctypes.byref(L), 2, 0, ok3, buf, NULL) == INV             # direction
+    assert pk(ctypes.byref(L), 0, 3, ok3, buf, NULL) == INV             # rank
+    assert pk(ctypes.byref(L), 0, 0, None, buf, NULL) == INV
+    assert pk(ctypes.byref(L), 0, 0, _planes(A, 0, A + 8192), buf, NULL) == INV
+    assert pk(ctypes.byref(L), 0, 0, ok3, NULL, NULL) == INV
+    assert pk(ctypes.byref(L), 0, 0, _planes(A + 1, A + 4096, A + 8192), buf, NULL) == UNS
+    assert pk(ctypes.byref(L), 0, 0, ok3, P(A + 4096), NULL) == INV     # overlap
+    assert up(ctypes.byref(L), 0, 0, NULL, ok3, NULL) == INV
+    assert up(ctypes.byref(L), 0, 0, buf, _planes(A, A, A + 8192), NULL) == INV  # outputs overlap
+    bad = _lib.DitA2AUnevenLayout.from_buffer_copy(L)
+    bad.seq_offsets[1] += 1                                             # tampered derived field
+    assert pk(ctypes.byref(bad), 0, 0, ok3, buf, NULL) == INV
+    assert "derived" in lib.dit_last_error().decode()
+    bad = _lib.DitA2AUnevenLayout.from_buffer_copy(L)
+    bad.U = 99
+    assert pk(ctypes.byref(bad), 0, 0, ok3, buf, NULL) == INV
+    huge = _uneven(lib, 1, 2**21, 1024, 128, 2, 1, 0)                   # >= 2^31 elements
+    assert pk(ctypes.byref(huge), 0, 0, ok3, buf, NULL) == UNS
+    many = _uneven(lib, 30000, 4, 2, 8, 2, 3, 0)                        # B * n_planes > 65535
+    assert pk(ctypes.byref(many), 0, 0, ok3, buf, NULL) == UNS
+    # rank 1 holds no rows: its sequence-to-head pack and head-to-sequence unpack are empty
+    assert pk(ctypes.byref(L), 0, 1, _planes(0, 0, 0), NULL, NULL) == 0
+    assert up(ctypes.byref(L), 1, 1, NULL, _planes(0, 0, 0), NULL) == 0
+
+
+def test_ring_anything_rejects(lib):
+    L = _uneven(lib, 2, 9, 2, 8, 3, 1, 0, [4, 0, 5])
+    pad, trim = lib.dit_ring_anything_pad, lib.dit_ring_anything_trim
+    one = _planes(A, 0, 0)
+    assert pad(None, 0, one, P(A + 65536), NULL) == INV
+    assert pad(ctypes.byref(L), 3, one, P(A + 65536), NULL) == INV      # rank
+    assert pad(ctypes.byref(L), 0, one, NULL, NULL) == INV
+    assert pad(ctypes.byref(L), 0, one, P(A + 64), NULL) == INV         # overlap
+    assert trim(ctypes.byref(L), NULL, one, NULL) == INV
+    assert trim(ctypes.byref(L), P(A + 65536), None, NULL) == INV
+    assert trim(None, P(A + 65536), one, NULL) == INV
+    empty = _uneven(lib, 0, 9, 2, 8, 3, 1, 0, [4, 0, 5])
+    assert trim(ctypes.byref(empty), NULL, _planes(0, 0, 0), NULL) == 0
