@@ -21,6 +21,11 @@ Sources (cited by page title and section):
 * cache-dit, "Context Parallelism" -- head padding before / after the
   all-to-all ("Any Head Num" under UAA); the padding-free splits of
   arbitrary sequence lengths and head counts (Ulysses Anything Attention).
+* cache-dit, "Context Parallelism" (Async FP8 Ulysses Attention) -- Q, V
+  and O exchanged as FP8, K kept in 16-bit; the FP8 format (OCP E4M3) and
+  the block scaling (32-element blocks with a power-of-two scale, as in the
+  OCP Microscaling formats) are readings (see the FP8 section of
+  ``reference``).
 * diffusers, "Distributed inference" (Ring Anything Attention) -- local K/V
   padded to the longest rank, gathered, then cut back to the real lengths.
 * The receive preparation with RoPE on Q and K (edge-dit.cpp "Parallel
@@ -60,6 +65,20 @@ from .reference import (  # noqa: F401
     all_to_all_uneven,
     ring_anything_pad,
     ring_anything_trim,
+    E4M3_MAX,
+    FP8_BLOCK,
+    e4m3_value,
+    e4m3_encode,
+    fp8_scale_exp,
+    quantize_fp8_blocks,
+    dequantize_fp8_blocks,
+    bf16_bits_to_f64,
+    f64_to_bf16_bits_exact,
+    fp8_chunk_sections,
+    pack_seq_to_head_fp8,
+    unpack_seq_to_head_fp8,
+    pack_head_to_seq_fp8,
+    unpack_head_to_seq_fp8,
     cfg_combine,
     cfg_combine_f32,
     fmaf,

@@ -452,6 +452,192 @@ def ring_anything_trim(gathered, seq_counts):
     return [x[i] for i in range(x.shape[0])]
 
 
+# -- FP8 Ulysses ------------------------------------------------------------------
+#
+# cache-dit "Context Parallelism" (Async FP8 Ulysses Attention): the
+# all-to-alls of Q, V and O move FP8 data, while K stays in 16-bit because
+# the softmax of Q K^T is sensitive to its precision.  The pages fix neither
+# the FP8 format nor the scaling.  Readings taken:
+#   * format: OCP 8-bit floating point E4M3 ("FN": bias 7, no infinities,
+#     largest finite 448, code 0x7F / 0xFF is NaN, subnormals m/8 * 2^-6);
+#   * scaling: one power-of-two scale per block of 32 consecutive elements
+#     of a head vector (the block size and E8M0 scale byte of the OCP
+#     Microscaling (MX) format), with the exponent chosen so that the block's
+#     largest magnitude fits: k = the smallest integer with
+#     amax <= 448 * 2^k, clamped to [-117, 126]; the scale byte is k + 127;
+#   * encoding: y = x * 2^-k (exact), code = y rounded to the nearest E4M3
+#     value, ties to the even code (mantissa LSB 0), sign kept (also of
+#     zero); decoding: value(code) * 2^k (exact in bf16 for k >= -117).
+
+
+E4M3_MAX = 448.0
+FP8_BLOCK = 32
+K_MIN, K_MAX = -117, 126
+
+
+def e4m3_value(code):
+    """Value of E4M3 codes (uint8 array) in float64; NaN for 0x7F / 0xFF."""
+    c = np.asarray(code).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS = e4m3_value(np.arange(0x7F))   # the 127 finite non-negative values, increasing
+
+
+def e4m3_encode(y):
+    """Codes of float64 values |y| <= 448: round to nearest, ties to even."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    assert np.all(a <= E4M3_MAX), "values beyond the largest finite E4M3 magnitude"
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)   # first value >= a
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_hi = _E4M3_POS[hi] - a
+    d_lo = a - _E4M3_POS[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi).astype(np.int64)
+    code = np.where(np.signbit(y), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def fp8_scale_exp(amax):
+    """Smallest integer k with amax <= 448 * 2^k, clamped to [K_MIN, K_MAX]."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, e = np.frexp(amax)                      # amax = m * 2^e, m in [0.5, 1)
+    # 448 * 2^(e-9) = 0.875 * 2^e: fits when m <= 0.875, else one more
+    k = np.where(m <= 0.875, e - 9, e - 8)
+    k = np.where(amax == 0, K_MIN, k)
+    return np.clip(k, K_MIN, K_MAX).astype(np.int64)
+
+
+def quantize_fp8_blocks(x):
+    """(codes uint8 [..., D], scale bytes uint8 [..., D/32]) of float64 x [..., D]."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    assert D % FP8_BLOCK == 0
+    blocks = x.reshape(x.shape[:-1] + (D // FP8_BLOCK, FP8_BLOCK))
+    k = fp8_scale_exp(np.max(np.abs(blocks), axis=-1))
+    y = blocks * np.exp2(-k.astype(np.float64))[..., None]
+    codes = e4m3_encode(y).reshape(x.shape)
+    return codes, (k + 127).astype(np.uint8)
+
+
+def dequantize_fp8_blocks(codes, scale_bytes):
+    """float64 values of block-scaled E4M3 codes [..., D]."""
+    codes = np.asarray(codes)
+    D = codes.shape[-1]
+    k = np.asarray(scale_bytes).astype(np.int64) - 127
+    v = e4m3_value(codes).reshape(codes.shape[:-1] + (D // FP8_BLOCK, FP8_BLOCK))
+    return (v * np.exp2(k.astype(np.float64))[..., None]).reshape(codes.shape)
+
+
+def bf16_bits_to_f64(bits):
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits_exact(x):
+    """bf16 bit patterns of values that bf16 represents exactly (asserted)."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(x, dtype=np.float64), equal_nan=True)
+    u = f.view(np.uint32)
+    assert not np.any(u & 0xFFFF), "not a bf16 value"
+    return (u >> 16).astype(np.uint16).view(np.int16)
+
+
+def fp8_chunk_sections(L, seq_to_head):
+    """Byte offsets of the sections of one peer's chunk and the chunk stride.
+
+    Sequence to head (planes Q, K, V): Q codes, V codes, K (bf16), Q scale
+    bytes, V scale bytes.  Head to sequence (plane O): O codes, O scale
+    bytes.  E = B * S_loc * H_loc * D elements per plane; the stride rounds
+    the chunk up to a multiple of 256 bytes, the tail bytes being zero.
+    """
+    E = L["B"] * L["S_loc"] * L["H_loc"] * L["D"]
+    if seq_to_head:
+        sec = dict(q=0, v=E, k=2 * E, q_scale=4 * E, v_scale=4 * E + E // 32)
+        used = 4 * E + E // 16
+    else:
+        sec = dict(o=0, o_scale=E)
+        used = E + E // 32
+    stride = -(-used // 256) * 256
+    return sec, used, stride
+
+
+def pack_seq_to_head_fp8(q_bits, k_bits, v_bits, L, rank):
+    """FP8 sequence-to-head send buffer (uint8 [U, stride]) of rank ``rank``:
+    the padded pack of each plane (pad rows / heads zero), Q and V encoded
+    by block, K kept as bf16 bit patterns.  Inputs: bf16 bits [B, S_loc, H, D]."""
+    assert L["D"] % FP8_BLOCK == 0
+    L1 = dict(L, n_planes=1)
+    sec, used, stride = fp8_chunk_sections(L, True)
+    U, E = L["U"], L["B"] * L["S_loc"] * L["H_loc"] * L["D"]
+    out = np.zeros((U, stride), dtype=np.uint8)
+    planes = {}
+    for name, t in (("q", q_bits), ("k", k_bits), ("v", v_bits)):
+        planes[name] = pack_seq_to_head([t], L1, rank).reshape(U, E)      # bf16 bits
+    for p in range(U):
+        for name in ("q", "v"):
+            codes, sbytes = quantize_fp8_blocks(bf16_bits_to_f64(planes[name][p]).reshape(-1, L["D"]))
+            out[p, sec[name]:sec[name] + E] = codes.reshape(-1)
+            out[p, sec[name + "_scale"]:sec[name + "_scale"] + E // 32] = sbytes.reshape(-1)
+        out[p, sec["k"]:sec["k"] + 2 * E] = planes["k"][p].astype(np.int16).view(np.uint8)
+    return out
+
+
+def unpack_seq_to_head_fp8(recv, L, rank):
+    """[Q, K, V] bf16 bits [B, S, H_loc, D] from an FP8 sequence-to-head
+    receive buffer (uint8 [U, stride], chunk p from source p): Q and V
+    decoded, K copied; pad rows dropped as in the 16-bit map."""
+    sec, used, stride = fp8_chunk_sections(L, True)
+    U, E, D = L["U"], L["B"] * L["S_loc"] * L["H_loc"] * L["D"], L["D"]
+    recv = np.asarray(recv, dtype=np.uint8).reshape(U, stride)
+    L1 = dict(L, n_planes=1)
+    res = {}
+    for name in ("q", "v"):
+        chunks = []
+        for p in range(U):
+            codes = recv[p, sec[name]:sec[name] + E].reshape(-1, D)
+            sb = recv[p, sec[name + "_scale"]:sec[name + "_scale"] + E // 32].reshape(-1, D // 32)
+            chunks.append(f64_to_bf16_bits_exact(dequantize_fp8_blocks(codes, sb)).reshape(-1))
+        res[name] = unpack_seq_to_head(np.stack(chunks).reshape(-1), L1, rank)[0]
+    kk = np.ascontiguousarray(recv[:, sec["k"]:sec["k"] + 2 * E]).view(np.int16).reshape(-1)
+    res["k"] = unpack_seq_to_head(kk, L1, rank)[0]
+    return [res["q"], res["k"], res["v"]]
+
+
+def pack_head_to_seq_fp8(o_bits, L, rank):
+    """FP8 head-to-sequence send buffer (uint8 [U, stride]) of the attention
+    output O (bf16 bits [B, S, H_loc, D]): the padded pack, encoded by block."""
+    sec, used, stride = fp8_chunk_sections(L, False)
+    U, E, D = L["U"], L["B"] * L["S_loc"] * L["H_loc"] * L["D"], L["D"]
+    packed = pack_head_to_seq([o_bits], dict(L, n_planes=1), rank).reshape(U, E)
+    out = np.zeros((U, stride), dtype=np.uint8)
+    for p in range(U):
+        codes, sb = quantize_fp8_blocks(bf16_bits_to_f64(packed[p]).reshape(-1, D))
+        out[p, :E] = codes.reshape(-1)
+        out[p, sec["o_scale"]:sec["o_scale"] + E // 32] = sb.reshape(-1)
+    return out
+
+
+def unpack_head_to_seq_fp8(recv, L, rank):
+    """O bf16 bits [B, S_loc, H, D] from an FP8 head-to-sequence receive
+    buffer: decoded, pad heads dropped, this rank's pad rows zero."""
+    sec, used, stride = fp8_chunk_sections(L, False)
+    U, E, D = L["U"], L["B"] * L["S_loc"] * L["H_loc"] * L["D"], L["D"]
+    recv = np.asarray(recv, dtype=np.uint8).reshape(U, stride)
+    chunks = []
+    for p in range(U):
+        codes = recv[p, :E].reshape(-1, D)
+        sb = recv[p, sec["o_scale"]:sec["o_scale"] + E // 32].reshape(-1, D // 32)
+        chunks.append(f64_to_bf16_bits_exact(dequantize_fp8_blocks(codes, sb)).reshape(-1))
+    return unpack_head_to_seq(np.stack(chunks).reshape(-1), dict(L, n_planes=1), rank)[0]
+
+
 def all_to_all(sends):
     """The exchange itself (a test helper; the library never performs it).
 
