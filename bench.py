@@ -245,6 +245,41 @@ def side_measurements(torch, sa, workloads, reps=20):
                                              "GB/s": round(4 * kv_bytes / us / 1e3, 1),
                                              "frac_hbm_peak": round(4 * kv_bytes / us / 1e3 / PEAK_HBM_GBPS, 4)}
     del bufs
+    # FP8 exchange at the FLUX U=2 shape: Q, V (and O) as block-scaled E4M3,
+    # K bf16; bytes are the planes read / written plus the FP8 buffer
+    L3 = sa.dit_a2a_layout_init(fw.B, fw.S, fw.H_total, fw.D, fw.U, 1, 3)
+    L1 = sa.dit_a2a_layout_init(fw.B, fw.S, fw.H_total, fw.D, fw.U, 1, 1)
+    st3 = sa.dit_a2a_fp8_bytes_per_peer(L3, sa.DIT_SEQ_TO_HEAD)
+    st1 = sa.dit_a2a_fp8_bytes_per_peer(L1, sa.DIT_HEAD_TO_SEQ)
+    shard_b = fw.B * L3.S_loc * fw.H_total * fw.D * 2
+    head_b = fw.B * fw.S * L3.H_loc * fw.D * 2
+    sets = max(2, math.ceil(2 * MALL_BYTES / (3 * shard_b + 3 * head_b + fw.U * (st3 + st1))) + 1)
+    bufs = []
+    for i in range(sets):
+        shard = [torch.empty((fw.B, L3.S_loc, fw.H_total, fw.D), dtype=torch.bfloat16, device="cuda").normal_()
+                 for _ in range(3)]
+        heads = [torch.empty((fw.B, fw.S, L3.H_loc, fw.D), dtype=torch.bfloat16, device="cuda").normal_()
+                 for _ in range(3)]
+        s3 = sa.dit_ulysses_pack_fp8(L3, sa.DIT_SEQ_TO_HEAD, 0, shard)
+        s1 = sa.dit_ulysses_pack_fp8(L1, sa.DIT_HEAD_TO_SEQ, 0, heads[:1])
+        bufs.append((shard, heads, s3, s1))
+    legs = {
+        "flux_fp8_pack_qkv": (3 * shard_b + fw.U * st3, lambda b: sa.dit_ulysses_pack_fp8(
+            L3, sa.DIT_SEQ_TO_HEAD, 0, b[0], send=b[2])),
+        "flux_fp8_unpack_qkv": (3 * head_b + fw.U * st3, lambda b: sa.dit_ulysses_unpack_fp8(
+            L3, sa.DIT_SEQ_TO_HEAD, 0, b[2], out=b[1])),
+        "flux_fp8_pack_o": (head_b + fw.U * st1, lambda b: sa.dit_ulysses_pack_fp8(
+            L1, sa.DIT_HEAD_TO_SEQ, 0, b[1][:1], send=b[3])),
+        "flux_fp8_unpack_o": (shard_b + fw.U * st1, lambda b: sa.dit_ulysses_unpack_fp8(
+            L1, sa.DIT_HEAD_TO_SEQ, 0, b[3], out=b[0][:1])),
+    }
+    for name, (moved, fn) in legs.items():
+        us = _time_launches(torch, lambda i, fn=fn: fn(bufs[i % sets]), reps)
+        res[name] = {"bytes": moved, "us": round(us, 2), "GB/s": round(moved / us / 1e3, 1),
+                     "frac_hbm_peak": round(moved / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    res["flux_fp8_exchange_bytes"] = {"qkv_fp8": fw.U * st3, "qkv_bf16": fw.U * L3.elems_per_peer * 2,
+                                      "o_fp8": fw.U * st1, "o_bf16": fw.U * L1.elems_per_peer * 2}
+    del bufs
     # hipMemcpy-class device copy of the same bytes, as the achievable-copy reference
     n_bytes = 2 * 96_768_000 // 2
     src = [torch.empty(n_bytes // 2, dtype=torch.bfloat16, device="cuda") for _ in range(6)]

@@ -13,6 +13,8 @@
  *                                          (no padding)
  *   dit_ring_anything_pad / _trim          equal-size K/V gather of uneven
  *                                          sequence shards
+ *   dit_ulysses_pack_fp8 / _unpack_fp8     the Ulysses maps with Q, V and O
+ *                                          exchanged as FP8 (K kept bf16)
  *   dit_attn_fwd                           attention with per-row LSE
  *   dit_attn_fwd_kvlen                     ... over a per-batch key prefix
  *   dit_attn_merge                         online-softmax merge of partial
@@ -192,6 +194,49 @@ dit_status_t dit_ulysses_unpack(const dit_a2a_layout* layout, dit_a2a_dir_t dir,
 dit_status_t dit_ulysses_unpack_rope(const dit_a2a_layout* layout, int32_t rank, const void* recv_buf,
                                      void* const* out_planes, const float* rope_cos,
                                      const float* rope_sin, void* stream);
+
+/*
+ * FP8 exchange (cache-dit "Context Parallelism", Async FP8 Ulysses
+ * Attention: Q, V and O cross the all-to-alls as FP8, K stays 16-bit because
+ * the softmax of Q K^T is sensitive to its precision).  The pages give no
+ * format or scaling; this library's encoding is:
+ *   - OCP E4M3 ("FN": bias 7, largest finite 448, no infinities);
+ *   - one power-of-two scale per block of 32 consecutive elements of a head
+ *     vector (the OCP Microscaling block size, E8M0 scale byte): k is the
+ *     smallest integer with max|x| <= 448 * 2^k over the block, clamped to
+ *     [-117, 126]; scale byte = k + 127;
+ *   - code = round-to-nearest-even E4M3 of x * 2^-k (sign kept, also of
+ *     zero); decoding gives value(code) * 2^k, which bf16 holds exactly.
+ *   Per element |decoded - x| <= max(2^-4 |x|, 2^(k-10)).
+ * The maps around the codes are those of dit_ulysses_pack / _unpack for the
+ * same layout (pad rows and heads encode as zeros; pad rows are dropped at
+ * the sequence-to-head unpack; pad heads are dropped and this rank's pad
+ * rows zeroed at the head-to-sequence unpack).
+ *
+ * Layout requirements: dtype bf16, D a multiple of 32; DIT_SEQ_TO_HEAD takes
+ * n_planes = 3 (planes Q, K, V, in that order), DIT_HEAD_TO_SEQ n_planes = 1
+ * (plane O).  Plane pointers and the buffer are 16-byte aligned.
+ *
+ * Buffers hold U chunks of dit_a2a_fp8_bytes_per_peer() bytes (chunk p for
+ * / from peer p).  With E = B * S_loc * H_loc * D, a chunk is, in bytes:
+ *   DIT_SEQ_TO_HEAD: Q codes [0, E), V codes [E, 2E), K bf16 [2E, 4E),
+ *                    Q scale bytes [4E, 4E + E/32), V scale bytes
+ *                    [4E + E/32, 4E + E/16);
+ *   DIT_HEAD_TO_SEQ: O codes [0, E), O scale bytes [E, E + E/32);
+ * codes and K in the element order [B, S_loc, H_loc, D] of the 16-bit
+ * chunk, scale byte i covering elements [32 i, 32 i + 32); zero bytes pad
+ * the chunk to a multiple of 256.  Sequence to head moves 4E + E/16 bytes
+ * per peer instead of 6E; head to sequence E + E/32 instead of 2E.
+ *
+ * Errors: INVALID_ARGUMENT (as dit_ulysses_pack, plus a wrong n_planes for
+ * the direction); UNSUPPORTED (dtype, D, alignment, size limits); HIP.
+ */
+dit_status_t dit_a2a_fp8_bytes_per_peer(const dit_a2a_layout* layout, dit_a2a_dir_t dir,
+                                        int64_t* bytes);
+dit_status_t dit_ulysses_pack_fp8(const dit_a2a_layout* layout, dit_a2a_dir_t dir, int32_t rank,
+                                  const void* const* in_planes, void* send_buf, void* stream);
+dit_status_t dit_ulysses_unpack_fp8(const dit_a2a_layout* layout, dit_a2a_dir_t dir, int32_t rank,
+                                    const void* recv_buf, void* const* out_planes, void* stream);
 
 /* Largest Ulysses (or ring) degree of the per-rank count layouts. */
 #define DIT_MAX_RANKS 64

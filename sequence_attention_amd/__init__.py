@@ -31,6 +31,7 @@ __all__ = [
     "dit_a2a_uneven_init", "dit_a2a_uneven_sizes", "dit_ulysses_pack_uneven",
     "dit_ulysses_unpack_uneven", "dit_ring_anything_pad", "dit_ring_anything_trim",
     "DitA2AUnevenLayout",
+    "dit_a2a_fp8_bytes_per_peer", "dit_ulysses_pack_fp8", "dit_ulysses_unpack_fp8",
     "dit_attn_fwd", "dit_attn_fwd_kvlen", "dit_attn_merge", "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
@@ -235,6 +236,43 @@ def dit_ring_anything_trim(layout: DitA2AUnevenLayout, gathered, out=None, strea
     out = list(out)
     check(lib().dit_ring_anything_trim(ctypes.byref(layout), _dev(gathered, "gathered"),
                                        _plane_ptrs(out, "out"), _stream(stream)), "dit_ring_anything_trim")
+    return out
+
+
+def dit_a2a_fp8_bytes_per_peer(layout: DitA2ALayout, direction: int) -> int:
+    """Bytes of one peer's chunk of the FP8 exchange buffer."""
+    n = ctypes.c_int64()
+    check(lib().dit_a2a_fp8_bytes_per_peer(ctypes.byref(layout), direction, ctypes.byref(n)),
+          "dit_a2a_fp8_bytes_per_peer")
+    return n.value
+
+
+def dit_ulysses_pack_fp8(layout: DitA2ALayout, direction: int, rank: int, planes, send=None, stream=None):
+    """FP8 send buffer (uint8 [U, bytes_per_peer]) from bf16 planes: [q, k, v]
+    shards for DIT_SEQ_TO_HEAD, [o] for DIT_HEAD_TO_SEQ."""
+    torch = _torch()
+    planes = list(planes)
+    if len(planes) != layout.n_planes:
+        raise ValueError(f"expected {layout.n_planes} planes, got {len(planes)}")
+    if send is None:
+        send = torch.empty((layout.U, dit_a2a_fp8_bytes_per_peer(layout, direction)), dtype=torch.uint8,
+                           device=planes[0].device)
+    check(lib().dit_ulysses_pack_fp8(ctypes.byref(layout), direction, rank, _plane_ptrs(planes, "planes"),
+                                     _dev(send, "send"), _stream(stream)), "dit_ulysses_pack_fp8")
+    return send
+
+
+def dit_ulysses_unpack_fp8(layout: DitA2ALayout, direction: int, rank: int, recv, out=None, stream=None):
+    """bf16 planes from an FP8 receive buffer: [q, k, v] of [B, S, H_loc, D]
+    for DIT_SEQ_TO_HEAD, [o] of [B, S_loc, H, D] for DIT_HEAD_TO_SEQ."""
+    torch = _torch()
+    if out is None:
+        shape = ((layout.B, layout.S, layout.H_loc, layout.D) if direction == DIT_SEQ_TO_HEAD
+                 else (layout.B, layout.S_loc, layout.H, layout.D))
+        out = [torch.empty(shape, dtype=torch.bfloat16, device=recv.device) for _ in range(layout.n_planes)]
+    out = list(out)
+    check(lib().dit_ulysses_unpack_fp8(ctypes.byref(layout), direction, rank, _dev(recv, "recv"),
+                                       _plane_ptrs(out, "out"), _stream(stream)), "dit_ulysses_unpack_fp8")
     return out
 
 

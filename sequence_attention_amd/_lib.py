@@ -40,6 +40,9 @@ EXPORTS = (
     "dit_ulysses_unpack_uneven",
     "dit_ring_anything_pad",
     "dit_ring_anything_trim",
+    "dit_a2a_fp8_bytes_per_peer",
+    "dit_ulysses_pack_fp8",
+    "dit_ulysses_unpack_fp8",
     "dit_attn_fwd",
     "dit_attn_fwd_kvlen",
     "dit_attn_merge",
@@ -137,6 +140,14 @@ def _declare(lib):
     lib.dit_ring_anything_pad.argtypes = [_UL, _I32, ctypes.POINTER(_P), _P, _P]
     lib.dit_ring_anything_trim.restype = ctypes.c_int
     lib.dit_ring_anything_trim.argtypes = [_UL, _P, ctypes.POINTER(_P), _P]
+    lib.dit_a2a_fp8_bytes_per_peer.restype = ctypes.c_int
+    lib.dit_a2a_fp8_bytes_per_peer.argtypes = [ctypes.POINTER(DitA2ALayout), ctypes.c_int, _I64P]
+    lib.dit_ulysses_pack_fp8.restype = ctypes.c_int
+    lib.dit_ulysses_pack_fp8.argtypes = [ctypes.POINTER(DitA2ALayout), ctypes.c_int, _I32,
+                                         ctypes.POINTER(_P), _P, _P]
+    lib.dit_ulysses_unpack_fp8.restype = ctypes.c_int
+    lib.dit_ulysses_unpack_fp8.argtypes = [ctypes.POINTER(DitA2ALayout), ctypes.c_int, _I32, _P,
+                                           ctypes.POINTER(_P), _P]
     lib.dit_attn_fwd.restype = ctypes.c_int
     lib.dit_attn_fwd.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                      ctypes.c_int, _P]

@@ -516,6 +516,108 @@ dit_status_t dit_ring_anything_trim(const dit_a2a_uneven_layout* L, const void* 
 
 namespace {
 
+// ---- FP8 exchange --------------------------------------------------------------
+
+// Bytes of one peer's FP8 chunk: `used` holds the sections, `stride` rounds
+// it up to a multiple of 256.
+void fp8_chunk_bytes(const dit_a2a_layout* L, int dir, int64_t* used, int64_t* stride) {
+  const int64_t E = (int64_t)L->B * L->S_loc * L->H_loc * L->D;
+  *used = dir == DIT_SEQ_TO_HEAD ? 4 * E + E / 16 : E + E / 32;
+  *stride = (*used + 255) / 256 * 256;
+}
+
+dit_status_t check_fp8(const dit_a2a_layout* L, int dir, int32_t rank) {
+  dit_status_t st = check_permute(L, dir, rank);
+  if (st != DIT_OK) return st;
+  if (L->dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "the FP8 exchange takes bf16 planes");
+  if (L->D % 32 != 0)
+    return fail(DIT_ERR_UNSUPPORTED, "head dim %d is not a multiple of the 32-element scale block", L->D);
+  const int want = dir == DIT_SEQ_TO_HEAD ? 3 : 1;
+  if (L->n_planes != want)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "the FP8 %s exchange takes n_planes = %d (got %d)",
+                dir == DIT_SEQ_TO_HEAD ? "sequence-to-head (Q, K, V)" : "head-to-sequence (O)", want,
+                L->n_planes);
+  int64_t used, stride;
+  fp8_chunk_bytes(L, dir, &used, &stride);
+  if (stride * L->U >= ((int64_t)1 << 40))
+    return fail(DIT_ERR_UNSUPPORTED, "FP8 exchange buffer too large");
+  return DIT_OK;
+}
+
+dit_status_t run_fp8(const dit_a2a_layout* L, int dir, int32_t rank, bool pack, const void* const* planes,
+                     const void* buf, void* stream) {
+  dit_status_t st = check_fp8(L, dir, rank);
+  if (st != DIT_OK) return st;
+  int64_t used, stride;
+  fp8_chunk_bytes(L, dir, &used, &stride);
+  const int64_t buf_bytes = stride * L->U;
+  const int64_t plane_elems =
+      dir == DIT_SEQ_TO_HEAD
+          ? (pack ? (int64_t)L->B * L->S_loc * L->H * L->D : (int64_t)L->B * L->S * L->H_loc * L->D)
+          : (pack ? (int64_t)L->B * L->S * L->H_loc * L->D : (int64_t)L->B * L->S_loc * L->H * L->D);
+  if (buf_bytes == 0 && plane_elems == 0) {
+    clear_error();
+    return DIT_OK;
+  }
+  const char* side = pack ? "in_planes" : "out_planes";
+  if (planes == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "%s array is NULL", side);
+  for (int i = 0; i < L->n_planes; ++i) {
+    if (plane_elems > 0 && planes[i] == nullptr)
+      return fail(DIT_ERR_INVALID_ARGUMENT, "%s[%d] is NULL", side, i);
+    if (!aligned(planes[i], 16)) return fail(DIT_ERR_UNSUPPORTED, "%s[%d] must be 16-byte aligned", side, i);
+  }
+  if (buf_bytes > 0 && buf == nullptr)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "%s is NULL", pack ? "send_buf" : "recv_buf");
+  if (!aligned(buf, 16)) return fail(DIT_ERR_UNSUPPORTED, "the FP8 exchange buffer must be 16-byte aligned");
+  const size_t pb = (size_t)plane_elems * 2;
+  for (int i = 0; i < L->n_planes; ++i) {
+    if (overlap(planes[i], pb, buf, (size_t)buf_bytes))
+      return fail(DIT_ERR_INVALID_ARGUMENT, "plane %d overlaps the exchange buffer", i);
+    if (!pack)
+      for (int j = i + 1; j < L->n_planes; ++j)
+        if (overlap(planes[i], pb, planes[j], pb))
+          return fail(DIT_ERR_INVALID_ARGUMENT, "output planes %d and %d overlap", i, j);
+  }
+  dit::Fp8PermuteArgs a;
+  for (int i = 0; i < 3; ++i) a.planes[i] = i < L->n_planes ? planes[i] : nullptr;
+  a.buf = buf;
+  a.stride = stride;
+  a.used = used;
+  a.B = L->B; a.S = L->S; a.H = L->H; a.D = L->D; a.U = L->U; a.S_loc = L->S_loc; a.H_loc = L->H_loc;
+  a.rank = rank;
+  const dit::PermuteKind kind =
+      dir == DIT_SEQ_TO_HEAD ? (pack ? dit::PACK_SEQ_TO_HEAD : dit::UNPACK_SEQ_TO_HEAD)
+                             : (pack ? dit::PACK_HEAD_TO_SEQ : dit::UNPACK_HEAD_TO_SEQ);
+  st = hip_status(dit::launch_fp8_permute(kind, a, (hipStream_t)stream), "FP8 permute launch");
+  if (st == DIT_OK) clear_error();
+  return st;
+}
+
+}  // namespace
+
+dit_status_t dit_a2a_fp8_bytes_per_peer(const dit_a2a_layout* L, dit_a2a_dir_t dir, int64_t* bytes) {
+  if (bytes == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  const dit_status_t st = check_fp8(L, (int)dir, 0);
+  if (st != DIT_OK) return st;
+  int64_t used, stride;
+  fp8_chunk_bytes(L, (int)dir, &used, &stride);
+  *bytes = stride;
+  clear_error();
+  return DIT_OK;
+}
+
+dit_status_t dit_ulysses_pack_fp8(const dit_a2a_layout* L, dit_a2a_dir_t dir, int32_t rank,
+                                  const void* const* in_planes, void* send_buf, void* stream) {
+  return run_fp8(L, (int)dir, rank, true, in_planes, send_buf, stream);
+}
+
+dit_status_t dit_ulysses_unpack_fp8(const dit_a2a_layout* L, dit_a2a_dir_t dir, int32_t rank,
+                                    const void* recv_buf, void* const* out_planes, void* stream) {
+  return run_fp8(L, (int)dir, rank, false, (const void* const*)out_planes, recv_buf, stream);
+}
+
+namespace {
+
 // dit_attn_fwd and dit_attn_fwd_merge: one validation path; `merge` makes
 // (o, lse) an accumulator that this call merges into.
 dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,

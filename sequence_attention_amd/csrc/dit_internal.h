@@ -88,6 +88,20 @@ struct ChunkCopyArgs {
 
 hipError_t launch_chunk_copy(const ChunkCopyArgs& a, hipStream_t stream);
 
+// FP8 Ulysses maps (bf16 planes <-> block-scaled E4M3 chunks, K kept bf16).
+// planes: PACK inputs / UNPACK outputs (sequence to head: Q, K, V; head to
+// sequence: O); buf: the send (PACK) or receive (UNPACK) buffer of U chunks
+// of `stride` bytes, the first `used` bytes of each holding the sections.
+// D is a multiple of 32, all pointers 16-byte aligned.
+struct Fp8PermuteArgs {
+  const void* planes[3];
+  const void* buf;
+  int64_t stride, used;
+  int32_t B, S, H, D, U, S_loc, H_loc, rank;
+};
+
+hipError_t launch_fp8_permute(PermuteKind kind, const Fp8PermuteArgs& a, hipStream_t stream);
+
 // Sequence-to-head unpack with RoPE on planes 0 and 1 (Q, K); plane 2 copied.
 struct RopeUnpackArgs {
   const void* recv;    // [U, n_planes, B, S_loc, H_loc, D]

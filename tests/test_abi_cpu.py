@@ -376,3 +376,45 @@ def test_ring_anything_rejects(lib):
     assert trim(None, P(A + 65536), one, NULL) == INV
     empty = _uneven(lib, 0, 9, 2, 8, 3, 1, 0, [4, 0, 5])
     assert trim(ctypes.byref(empty), NULL, _planes(0, 0, 0), NULL) == 0
+
+
+# ---- FP8 exchange ----------------------------------------------------------------
+
+@pytest.mark.parametrize("args,dirn", [((1, 4608, 24, 128, 2, 1, 3), 0), ((2, 37, 5, 64, 3, 1, 3), 0),
+                                       ((1, 4608, 24, 128, 2, 1, 1), 1), ((1, 10, 4, 32, 4, 1, 1), 1)])
+def test_fp8_bytes_per_peer_matches_oracle(lib, args, dirn):
+    L = _layout(lib, *args, 0)
+    n = ctypes.c_int64()
+    assert lib.dit_a2a_fp8_bytes_per_peer(ctypes.byref(L), dirn, ctypes.byref(n)) == 0
+    Lo = oracle.a2a_layout(*args)
+    assert n.value == oracle.fp8_chunk_sections(Lo, dirn == 0)[2]
+
+
+def test_fp8_rejects(lib):
+    L3 = _layout(lib, 1, 8, 4, 32, 2, 1, 3, 0)
+    L1 = _layout(lib, 1, 8, 4, 32, 2, 1, 1, 0)
+    ok3 = _planes(A, A + 8192, A + 16384)
+    buf = P(A + 65536)
+    pk, up = lib.dit_ulysses_pack_fp8, lib.dit_ulysses_unpack_fp8
+    n = ctypes.c_int64()
+    assert lib.dit_a2a_fp8_bytes_per_peer(ctypes.byref(L3), 0, None) == INV
+    assert lib.dit_a2a_fp8_bytes_per_peer(ctypes.byref(L3), 1, ctypes.byref(n)) == INV   # O needs n_planes 1
+    assert pk(None, 0, 0, ok3, buf, NULL) == INV
+    assert pk(ctypes.byref(L1), 0, 0, ok3, buf, NULL) == INV          # Q, K, V need n_planes 3
+    assert pk(ctypes.byref(L3), 1, 0, ok3, buf, NULL) == INV          # O needs n_planes 1
+    assert pk(ctypes.byref(L3), 0, 2, ok3, buf, NULL) == INV          # rank
+    assert pk(ctypes.byref(L3), 0, 0, None, buf, NULL) == INV
+    assert pk(ctypes.byref(L3), 0, 0, _planes(A, 0, A + 16384), buf, NULL) == INV
+    assert pk(ctypes.byref(L3), 0, 0, ok3, NULL, NULL) == INV
+    assert pk(ctypes.byref(L3), 0, 0, _planes(A + 8, A + 8192, A + 16384), buf, NULL) == UNS
+    assert pk(ctypes.byref(L3), 0, 0, ok3, P(A + 65536 + 8), NULL) == UNS
+    assert pk(ctypes.byref(L3), 0, 0, ok3, P(A + 8192), NULL) == INV  # overlap
+    assert up(ctypes.byref(L1), 1, 0, buf, None, NULL) == INV
+    assert up(ctypes.byref(L3), 0, 0, NULL, ok3, NULL) == INV
+    assert up(ctypes.byref(L3), 0, 0, buf, _planes(A, A, A + 16384), NULL) == INV   # outputs overlap
+    f32 = _layout(lib, 1, 8, 4, 32, 2, 1, 3, 2)
+    assert pk(ctypes.byref(f32), 0, 0, ok3, buf, NULL) == UNS         # bf16 only
+    d16 = _layout(lib, 1, 8, 4, 16, 2, 1, 3, 0)
+    assert pk(ctypes.byref(d16), 0, 0, ok3, buf, NULL) == UNS         # D not a multiple of 32
+    empty = _layout(lib, 0, 8, 4, 32, 2, 1, 3, 0)
+    assert pk(ctypes.byref(empty), 0, 0, _planes(0, 0, 0), NULL, NULL) == 0
