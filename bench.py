@@ -57,8 +57,8 @@ CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches 
 # Valid only for the kernel source they were taken on (SHA-256 below); any
 # change to that file reports traffic as null until the counters are re-taken.
 ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
-ATTN_TRAFFIC = {"src_sha256": "4e76bf22a6a106cf902c72c12589c4f856df1a585fda1401a48f702869e09bf2",
-                "workload": "flux", "fetch_bytes": 52_214_784, "write_bytes": 14_428_416}
+ATTN_TRAFFIC = {"src_sha256": "54f5e5f29f4c931fd628de5d243bc1074b1d55bffb18913786e25e79bff495e7",
+                "workload": "flux", "fetch_bytes": 52_216_832, "write_bytes": 14_377_024}
 
 
 def parse():
