@@ -57,7 +57,7 @@ CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches 
 # Valid only for the kernel source they were taken on (SHA-256 below); any
 # change to that file reports traffic as null until the counters are re-taken.
 ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
-ATTN_TRAFFIC = {"src_sha256": "54f5e5f29f4c931fd628de5d243bc1074b1d55bffb18913786e25e79bff495e7",
+ATTN_TRAFFIC = {"src_sha256": "3aa960c5b509104b0a5a0cff5b3c3fc37d05e589d395b040d7faad06f6c9a042",
                 "workload": "flux", "fetch_bytes": 52_216_832, "write_bytes": 14_377_024}
 
 
