@@ -32,9 +32,14 @@
 //  * Softmax runs in fp32 with exp2 and scale*log2(e) folded into one FMA.
 //    The running max is only raised when a block's max exceeds it by more
 //    than 2^8 in the exp2 domain (a wave-uniform branch), so the O rescale
-//    is rare; P then stays <= 256, exact enough in bf16 and far from fp32
-//    limits.  Tail keys past Skv are clamped on load and masked to -inf;
-//    tail query rows are never stored.
+//    is rare; P then stays <= 256, far from fp32 limits.  The PV product
+//    uses P rounded to bf16, so O is normalised by the sum of those rounded
+//    weights (a consistent weighted average of V rows): with the lazy
+//    rescale the dominant weight of a near one-hot row is not exactly 1, and
+//    normalising by the unrounded sum would leave its rounding error
+//    (2^-9 |v|) in O.  LSE takes the sum of the unrounded weights.  Tail
+//    keys past Skv are clamped on load and masked to -inf; tail query rows
+//    are never stored.
 //  * Work tiles are renumbered so that consecutive query tiles of one head
 //    land on the same XCD (workgroups are dealt round-robin over the 8
 //    XCDs): the head's K/V stream is then served from that XCD's L2.
@@ -47,11 +52,11 @@ namespace dit {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 8;
@@ -112,10 +117,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Floats of one partial-result slot: per lane the D/2 accumulator registers
-// of O^T, then the running max and the lane's share of the row sum.
+// of O^T, then the running max, the lane's share of the row sum and of the
+// rounded-weight sum, and one unused float (16 bytes per lane).
 template <int D>
 constexpr size_t slot_floats() {
-  return (size_t)kWaves * 64 * (D / 2 + 2);
+  return (size_t)kWaves * 64 * (D / 2 + 4);
 }
 
 template <int D, bool kOutF32, bool kMerge>
@@ -245,7 +251,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
     float m_used = -INFINITY;  // running reference max of raw scores q . k
-    float lsum = 0.0f;         // this lane's share of the row sum
+    float lsum = 0.0f;         // this lane's share of the row sum (for LSE)
+    float lsum_r = 0.0f;       // ... of the bf16-rounded weights (normalises O)
 
     // one key block from stage ST; block kb + 3 is streamed into stage ST - 1
     auto block = [&](auto stage, int kb) __attribute__((always_inline)) {
@@ -314,6 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         const float m_new = raise ? mx : m_used;
         const float alpha = __builtin_amdgcn_exp2f((m_used - m_new) * c);
         lsum *= alpha;
+        lsum_r *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -333,6 +341,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
           lsum += pr;
           pb[t][r >> 3][r & 7] = (__bf16)pr;
         }
+      {
+        // sum of the rounded weights, two per v_dot2 with (1, 1)
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2 pair = {pb[t][hh][e], pb[t][hh][e + 1]};
+              lsum_r = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum_r, false);
+            }
+      }
 
       // O^T += V^T P^T: 4 key steps of 16 keys
 #pragma unroll
@@ -396,14 +417,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     // an accumulator with L_a = -inf holds no keys and is replaced.  The two
     // lanes of a row read the old LSE before the first of them writes it
     // (same wave, program order).
-    auto store_out = [&](const f32x16 (&acc)[DT], float m_ref, float l_lane) __attribute__((always_inline)) {
+    auto store_out = [&](const f32x16 (&acc)[DT], float m_ref, float l_lane, float lr_lane)
+                         __attribute__((always_inline)) {
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       const float ltot = l_lane + __shfl_xor(l_lane, 32);
+      const float lrtot = lr_lane + __shfl_xor(lr_lane, 32);
       if (!q_ok) return;
       const size_t orow = ((size_t)b * p.Sq + q_row) * rs + (size_t)h * D;
       const size_t lse_idx = ((size_t)b * p.H + h) * p.Sq + q_row;
       const float l_c = m_ref * p.scale + __logf(ltot);
-      float cc = 1.0f / ltot, ca = 0.0f, l_new = l_c;
+      float cc = 1.0f / lrtot, ca = 0.0f, l_new = l_c;
       if constexpr (kMerge) {
         const float l_a = p.lse[lse_idx];
         if (l_a != -INFINITY) {
@@ -411,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
           const float wa = __expf(l_a - m), wc = __expf(l_c - m);
           const float den = wa + wc;
           ca = wa / den;
-          cc = wc / (den * ltot);
+          cc = wc / (den * lrtot);
           l_new = m + __logf(den);
         }
       }
@@ -450,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     };
 
     if (whole) {
-      store_out(oacc, m_used, lsum);
+      store_out(oacc, m_used, lsum, lsum_r);
     } else {
       // ---- split tile: publish this piece, the last piece to arrive merges --
       // The tile's pieces are the workgroups first .. first + split - 1 of
@@ -465,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       auto o_off = [&](int dt, int u) __attribute__((always_inline)) {
         return (int)((((dt * 4 + u) * kWaves + wave) * 64 + lane) * 16);
       };
-      const int ml_off = (int)(ML_OFF * sizeof(float)) + (wave * 64 + lane) * 8;
+      const int ml_off = (int)(ML_OFF * sizeof(float)) + (wave * 64 + lane) * 16;
       {
         const __amdgpu_buffer_rsrc_t sl = slot_of(j);
 #pragma unroll
@@ -475,8 +498,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
             const f32x4 v4 = {oacc[dt][4 * u], oacc[dt][4 * u + 1], oacc[dt][4 * u + 2], oacc[dt][4 * u + 3]};
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), sl, o_off(dt, u), 0, kScopeAgent);
           }
-        const u32x2 ml = {__float_as_uint(m_used), __float_as_uint(lsum)};
-        __builtin_amdgcn_raw_buffer_store_b64(ml, sl, ml_off, 0, kScopeAgent);
+        const u32x4 ml = {__float_as_uint(m_used), __float_as_uint(lsum), __float_as_uint(lsum_r), 0u};
+        __builtin_amdgcn_raw_buffer_store_b128(ml, sl, ml_off, 0, kScopeAgent);
       }
       // Slot traffic uses device-scope coherent accesses (they bypass the
       // XCD-private L2 state), so completion of this wave's stores is all the
@@ -494,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         // so the result does not depend on which piece arrived last
         float M = -INFINITY;
         for (uint32_t w = first; w < first + p.split; ++w) {
-          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(slot_of(w), ml_off, 0, kScopeAgent);
+          const u32x4 ml = __builtin_amdgcn_raw_buffer_load_b128(slot_of(w), ml_off, 0, kScopeAgent);
           M = fmaxf(M, __uint_as_float(ml[0]));
         }
         f32x16 acc[DT];
@@ -502,12 +525,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[dt][r] = 0.0f;
-        float l = 0.0f;
+        float l = 0.0f, lr = 0.0f;
         for (uint32_t w = first; w < first + p.split; ++w) {
           const __amdgpu_buffer_rsrc_t sl = slot_of(w);
-          const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(sl, ml_off, 0, kScopeAgent);
+          const u32x4 ml = __builtin_amdgcn_raw_buffer_load_b128(sl, ml_off, 0, kScopeAgent);
           const float alpha = __builtin_amdgcn_exp2f((__uint_as_float(ml[0]) - M) * c);
           l += alpha * __uint_as_float(ml[1]);
+          lr += alpha * __uint_as_float(ml[2]);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -518,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
               for (int e = 0; e < 4; ++e) acc[dt][4 * u + e] += alpha * v4[e];
             }
         }
-        store_out(acc, M, l);
+        store_out(acc, M, l, lr);
         if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }

@@ -7,11 +7,14 @@ LSE <= 1e-3; fp32 O and LSE <= 1e-5.  Because |O| is far below 1e-2 at
 long sequences, every bf16 case also bounds max|dO| / max|O| <= 2e-2 (bf16
 rounding of P and of O is ~2^-9 relative each).
 
-Stress inputs whose outputs reach |O| >= 2.56 ("sharp": near one-hot
-softmax picks single V rows) cannot meet an absolute 1e-2 in any bf16
-output: storing O alone costs half an ulp, 2^-8 |O|.  There the bound is
-1e-2 + 2^-8 |O_ref| per element (the stored-output rounding added to the
-absolute bound); the relative and LSE bounds are unchanged.
+The stress inputs ("sharp", "huge": near one-hot softmax picks single V
+rows) reach |O| above 4, where half the spacing of bf16 values (2^-7 on
+[4, 8)) exceeds 1e-2 by itself, so no bf16 output can promise an absolute
+1e-2 there.  For those cases only, each element's bound is 1e-2 plus the
+exact half-spacing of bf16 at |O_ref| + 1e-2 (the rounding of the stored
+value, taken at the largest magnitude the unrounded result may have); the
+relative and LSE bounds are unchanged.  Every other case, including the
+sharper-than-standard custom scale, keeps the plain 1e-2.
 """
 
 import math
@@ -44,6 +47,13 @@ def run_attn(q, k, v, scale=None, o_dtype=None, lse=True):
     return o.t, (l.t if lse else None)
 
 
+def bf16_half_spacing(x: np.ndarray) -> np.ndarray:
+    """Half the distance between adjacent bf16 values around |x| (8
+    significand bits): for |x| in [2^(E-1), 2^E) the spacing is 2^(E-8)."""
+    _, e = np.frexp(np.abs(x))
+    return np.where(x == 0, 0.0, np.ldexp(1.0, e - 9))
+
+
 def check(o, lse, q, k, v, scale, rows=None, dtype=torch.bfloat16, what="", out_rounding=False):
     ro, rl = oracle.attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), scale, rows=rows)
     go = o.float().cpu().numpy()
@@ -55,8 +65,9 @@ def check(o, lse, q, k, v, scale, rows=None, dtype=torch.bfloat16, what="", out_
     eo = max_abs(go, ro)
     assert np.all(np.isfinite(go)), f"{what}: non-finite O"
     if out_rounding:
-        excess = np.max(np.abs(go - ro) - (tol_o + 2.0 ** -8 * np.abs(ro)))
-        assert excess <= 0, f"{what}: O error exceeds 1e-2 + 2^-8|O| by {excess:.3e}"
+        bound = tol_o + bf16_half_spacing(np.abs(ro) + tol_o)
+        excess = np.max(np.abs(go - ro) - bound)
+        assert excess <= 0, f"{what}: O error exceeds 1e-2 + half a bf16 spacing by {excess:.3e}"
     else:
         assert eo <= tol_o, f"{what}: O max-abs {eo:.3e} > {tol_o}"
     if dtype == torch.bfloat16:
@@ -128,7 +139,8 @@ def test_stress_inputs(name, stress):
     q, k, v = workloads.attention_inputs(w, stress=stress, seed=3)
     o, lse = run_attn(q, k, v, w.scale)
     rows = None if name == "tiny" else np.arange(0, w.Sq, 7)
-    check(o, lse, q, k, v, w.scale, rows=rows, what=f"{name}/{stress}", out_rounding=True)
+    check(o, lse, q, k, v, w.scale, rows=rows, what=f"{name}/{stress}",
+          out_rounding=stress in ("sharp", "huge"))
 
 
 RAGGED = [
@@ -201,12 +213,13 @@ def test_run_twice_is_bitwise_identical():
 
 
 def test_custom_scale():
-    # scale 0.37 at D=64 makes scores ~3x sharper than 1/sqrt(D): a stress-like
-    # case where |O| passes 2.56, so the stored-output rounding is added
+    # scale 0.37 at D=64 makes scores ~3x sharper than 1/sqrt(D); |O| reaches
+    # 3.37, where storing bf16 alone costs up to 0.0076, and the plain 1e-2
+    # holds only if O is normalised consistently with the rounded weights
     w = workloads.WORKLOADS["tiny"]
     q, k, v = workloads.attention_inputs(w, seed=9)
     o, lse = run_attn(q, k, v, 0.37)
-    check(o, lse, q, k, v, 0.37, what="scale 0.37", out_rounding=True)
+    check(o, lse, q, k, v, 0.37, what="scale 0.37")
 
 
 # Shapes whose last round of tiles is cut into key chunks merged by the

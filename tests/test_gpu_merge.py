@@ -81,6 +81,43 @@ def test_commutative_bitwise():
     assert torch.equal(x, y) and torch.equal(xl, yl)
 
 
+def test_associative_fp32_within_1e_6():
+    # (a + b) + c against a + (b + c) on the fp32 path: the online-softmax
+    # merge is associative in exact arithmetic (SGLang "Parallelism
+    # Overview", the per-hop merge folds partial results in any grouping),
+    # so the two groupings may differ only by fp32 rounding.  O in [-1, 1]
+    # keeps an fp32 ulp at or below 2^-23; LSE ~ N(0, 2^2) with a few empty
+    # rows on each side.
+    log("merge associativity fp32")
+    B, Sq, H, D = 1, 700, 6, 128
+    g = torch.Generator().manual_seed(21)
+    parts = []
+    for i in range(3):
+        o = torch.rand(B, Sq, H, D, generator=g) * 2 - 1
+        lse = torch.randn(B, H, Sq, generator=g) * 2
+        lse[0, i, 5 * i:5 * i + 7] = -np.inf
+        parts.append((o, lse))
+    (oa, la), (ob, lb), (oc, lc) = parts
+    left, left_l = oa.to(DEV), la.to(DEV)
+    sa.dit_attn_merge(left, left_l, ob.to(DEV), lb.to(DEV))
+    sa.dit_attn_merge(left, left_l, oc.to(DEV), lc.to(DEV))
+    bc, bc_l = ob.to(DEV), lb.to(DEV)
+    sa.dit_attn_merge(bc, bc_l, oc.to(DEV), lc.to(DEV))
+    right, right_l = oa.to(DEV), la.to(DEV)
+    sa.dit_attn_merge(right, right_l, bc, bc_l)
+    torch.cuda.synchronize()
+    assert max_abs(left.cpu().numpy(), right.cpu().numpy()) <= 1e-6
+    ll, rl = left_l.cpu().numpy(), right_l.cpu().numpy()
+    assert np.array_equal(np.isneginf(ll), np.isneginf(rl))
+    fin = np.isfinite(ll)
+    # LSE compared relative to its magnitude (an fp32 ulp at |L| >= 8 is
+    # already 2^-20 ~ 9.5e-7)
+    assert np.all(np.abs(ll[fin] - rl[fin]) <= 1e-6 * np.maximum(1.0, np.abs(ll[fin])))
+    # and both equal the oracle's fold
+    ro, rlo = oracle.merge(*oracle.merge(oa.numpy(), la.numpy(), ob.numpy(), lb.numpy()), oc.numpy(), lc.numpy())
+    assert max_abs(left.cpu().numpy(), ro) <= 1e-6
+
+
 def ring_on_gpu(q, k, v, scale, R, order, acc_dtype):
     """The ring hop loop of one rank run as sequential chunks on one GPU."""
     Skv = k.shape[1]

@@ -181,3 +181,56 @@ def test_fp8_chunk_is_smaller_than_the_16bit_chunk():
     assert stride < 6 * E * 0.7                                          # vs 3 bf16 planes
     _, used_o, _ = oracle.fp8_chunk_sections(L, False)
     assert used_o == E + E // 32
+
+
+# Block membership: which 32 elements share one scale.  A head vector of 64
+# elements whose halves differ by 2^20 (and in sign) must give two distinct
+# scale bytes, each half encoded against its own scale.  First half:
+# x_j = (j + 1) / 8 for j = 0..31, so the block maximum is 4 and the
+# exponent is the smallest k with 4 <= 448 * 2^k, i.e. k = -6 (448 * 2^-7 =
+# 3.5 is too small), scale byte 121; the scaled values are y_j = 8 (j + 1) =
+# 8, 16, ..., 256.  Their E4M3 codes, worked out by hand from
+# value = (1 + m/8) * 2^(e - 7): 8 = 2^3 is e = 10, m = 0 (0x50); between 128
+# and 256 the spacing is 16, so the odd multiples of 8 there are ties that go
+# to the even mantissa (136 -> 128, 152 -> 160, 168 -> 160, 184 -> 192,
+# 200 -> 192, 216 -> 224, 232 -> 224, 248 -> 256).  Second half: -x * 2^20,
+# exponent 14 (scale byte 141), the same codes with the sign bit set.
+HAND_CODES = [
+    0x50, 0x58, 0x5C, 0x60, 0x62, 0x64, 0x66, 0x68,
+    0x69, 0x6A, 0x6B, 0x6C, 0x6D, 0x6E, 0x6F, 0x70,
+    0x70, 0x71, 0x72, 0x72, 0x72, 0x73, 0x74, 0x74,
+    0x74, 0x75, 0x76, 0x76, 0x76, 0x77, 0x78, 0x78,
+]
+
+
+def _grouping_pin_holds(quantize) -> bool:
+    first = np.arange(1, 33, dtype=np.float64) / 8.0
+    x = np.concatenate([first, -first * 2.0 ** 20])[None, None, :]     # one [1, 1, 64] head vector
+    codes, sb = quantize(x)
+    want_codes = np.array(HAND_CODES + [c | 0x80 for c in HAND_CODES], dtype=np.uint8)
+    return (sb.reshape(-1).tolist() == [121, 141]
+            and np.array_equal(codes.reshape(-1), want_codes))
+
+
+def test_block_membership_hand_table():
+    assert _grouping_pin_holds(oracle.quantize_fp8_blocks)
+    # the hand table is also what torch's E4M3 conversion gives for 8 (j + 1)
+    y = torch.arange(8.0, 257.0, 8.0, dtype=torch.float32)
+    assert torch.equal(y.to(torch.float8_e4m3fn).view(torch.uint8),
+                       torch.tensor(HAND_CODES, dtype=torch.uint8))
+
+
+def test_block_membership_pin_catches_a_strided_grouping():
+    # planted mistake: blocks taken as every other element (a strided
+    # reshape) instead of 32 consecutive ones; the pin must reject it
+    def strided(x):
+        x = np.asarray(x, dtype=np.float64)
+        D = x.shape[-1]
+        nb = D // oracle.FP8_BLOCK
+        blocks = np.swapaxes(x.reshape(x.shape[:-1] + (oracle.FP8_BLOCK, nb)), -1, -2)
+        k = oracle.fp8_scale_exp(np.max(np.abs(blocks), axis=-1))
+        y = blocks * np.exp2(-k.astype(np.float64))[..., None]
+        codes = np.swapaxes(oracle.e4m3_encode(y), -1, -2).reshape(x.shape)
+        return codes, (k + 127).astype(np.uint8)
+
+    assert not _grouping_pin_holds(strided)
