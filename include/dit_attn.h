@@ -15,7 +15,10 @@
  *                                          sequence shards
  *   dit_ulysses_pack_fp8 / _unpack_fp8     the Ulysses maps with Q, V and O
  *                                          exchanged as FP8 (K kept bf16)
- *   dit_attn_fwd                           attention with per-row LSE
+ *   dit_attn_fwd, dit_attn_fwd_ws          attention with per-row LSE (_ws:
+ *                                          with a caller workspace that lets
+ *                                          the kernel split the last round)
+ *   dit_attn_workspace_size                that workspace's size
  *   dit_attn_fwd_kvlen                     ... over a per-batch key prefix
  *   dit_attn_merge                         online-softmax merge of partial
  *                                          results (ring hops)
@@ -31,10 +34,11 @@
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers to contiguous row-major tensors,
- *     owned by the caller; the library never frees or retains them.  The
- *     only library-owned device memory is dit_attn_fwd's per-(device,
- *     stream) workspace (see there).  Thread-safe; the per-thread error
- *     text is the only other state.
+ *     owned by the caller; the library never allocates, frees or retains
+ *     device memory (a workspace, where an entry point takes one, is the
+ *     caller's too).  Thread-safe; the only state kept between calls is
+ *     the per-thread error text and per-device facts (compute-unit count,
+ *     kernel occupancy) queried once per device.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*,
  *     NULL = the default stream) and never synchronizes.
  *   - All validation happens before any launch; on an error nothing is
@@ -56,7 +60,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 1
+#define DIT_ABI_VERSION 2
 
 typedef enum {
   DIT_OK = 0,
@@ -365,21 +369,55 @@ dit_status_t dit_ring_anything_trim(const dit_a2a_uneven_layout* layout, const v
  *   identity of dit_attn_merge).
  * No aliasing between inputs and outputs.  Deterministic: a repeated call
  *   on the same device returns bitwise identical O and LSE.
- * Workspace: the bf16 path may cut query tiles into key chunks merged on
- *   the GPU; their partial results and per-tile arrival counters live in a
- *   workspace the library allocates (hipMalloc) on the first call on each
- *   (device, stream) that needs it, zero-fills on `stream`, grows when a
- *   larger call comes (after synchronizing `stream`) and keeps until the
- *   process ends (at most about 35 MB per stream on a 256-CU device).
- *   Calls on different streams never share it.  A first call on a stream
- *   therefore allocates and cannot be captured into a graph.
+ * Uses no memory beyond its arguments: every query tile is taken whole
+ *   (dit_attn_fwd_ws may be faster on shapes whose tiles do not fill the
+ *   last round of the device).
  * Errors: INVALID_ARGUMENT (null pointer of a non-empty tensor, negative
- * size, bad scale or dtype); UNSUPPORTED (D, dtype pair, alignment); HIP
- * (including a failed workspace allocation).
+ * size, bad scale or dtype); UNSUPPORTED (D, dtype pair, alignment); HIP.
  */
 dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                           int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
                           dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* stream);
+
+/*
+ * Bytes of workspace that dit_attn_fwd_ws (merge = 0) or dit_attn_fwd_merge
+ * (merge = 1) use for a call of these sizes on the CURRENT device (the
+ * device's compute-unit count decides how the work is cut).  0 means the
+ * call never splits a tile (fp32 path, empty calls, shapes that fill the
+ * device's rounds exactly).  Arguments as dit_attn_fwd.  For a bf16 call on a
+ * 256-CU device the size is at most 256 x 139264 + 1024 bytes (about
+ * 35.7 MB at D = 128).  Host-only apart from device attribute queries.
+ * Errors: INVALID_ARGUMENT (bytes NULL, negative size, bad dtype or merge),
+ * UNSUPPORTED (as dit_attn_fwd), HIP (no device).
+ */
+dit_status_t dit_attn_workspace_size(int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D,
+                                     dit_dtype_t in_dtype, dit_dtype_t o_dtype, int32_t merge,
+                                     int64_t* bytes);
+
+/*
+ * dit_attn_fwd with a caller-owned workspace.  When the query tiles do not
+ * fill the device's last round of resident workgroups, the bf16 path cuts
+ * that round's tiles into key chunks, one workgroup each; every chunk writes
+ * its unnormalised partial result to a workspace slot and the last chunk of
+ * a tile to arrive merges them (online-softmax rule, fixed key order, so
+ * the result stays deterministic).  Same results as dit_attn_fwd within the
+ * attention tolerance (not bitwise: the split changes the summation order).
+ *
+ * workspace: device memory of workspace_bytes bytes, 256-byte aligned,
+ *   whose first bytes (the arrival counters) are ZERO the first time it is
+ *   used (e.g. zero-filled once after allocation); every call leaves them
+ *   zero again.  NULL with workspace_bytes = 0: no split (= dit_attn_fwd).
+ *   workspace_bytes must be at least dit_attn_workspace_size() for the call.
+ *   Calls that may run at the same time (different streams) need different
+ *   workspaces; calls on one stream may share one.
+ * Errors: as dit_attn_fwd; INVALID_ARGUMENT also for a workspace smaller
+ * than needed, NULL with a nonzero size, or overlapping a tensor;
+ * UNSUPPORTED for a misaligned workspace.
+ */
+dit_status_t dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
+                             dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* workspace,
+                             int64_t workspace_bytes, void* stream);
 
 /*
  * Attention over a per-batch prefix of the keys: keys j >= kv_len[b] of
@@ -396,7 +434,7 @@ dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, 
  *   or leaves the accumulator unchanged (merge = 1).
  * Other arguments as dit_attn_fwd (merge = 0) or dit_attn_fwd_merge
  *   (merge = 1: o / lse are the accumulator, lse required).
- * Tiles are never split into key chunks on this path (no workspace use).
+ * Tiles are never split into key chunks on this path (no workspace).
  * Errors: as dit_attn_fwd; INVALID_ARGUMENT also for a NULL kv_len or
  * merge outside {0, 1}.
  */
@@ -443,13 +481,14 @@ dit_status_t dit_attn_merge(void* o_acc, float* lse_acc, const void* o_part,
  *   O = 0, LSE = -inf starts the hop loop).
  * Skv == 0: the chunk is empty, the accumulator is left unchanged.
  * No aliasing between q/k/v and the accumulator.  Deterministic.
- * Workspace: as dit_attn_fwd.
- * Errors: as dit_attn_fwd; INVALID_ARGUMENT also when lse_acc is NULL.
+ * workspace, workspace_bytes: as dit_attn_fwd_ws (size from
+ *   dit_attn_workspace_size with merge = 1); NULL and 0 for none.
+ * Errors: as dit_attn_fwd_ws; INVALID_ARGUMENT also when lse_acc is NULL.
  */
 dit_status_t dit_attn_fwd_merge(const void* q, const void* k, const void* v, void* o_acc,
                                 float* lse_acc, int32_t B, int32_t Sq, int32_t Skv, int32_t H,
                                 int32_t D, float scale, dit_dtype_t in_dtype, dit_dtype_t acc_dtype,
-                                void* stream);
+                                void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Classifier-free guidance combine (edge-dit.cpp "Parallel execution", CFG

@@ -44,6 +44,8 @@ EXPORTS = (
     "dit_ulysses_pack_fp8",
     "dit_ulysses_unpack_fp8",
     "dit_attn_fwd",
+    "dit_attn_workspace_size",
+    "dit_attn_fwd_ws",
     "dit_attn_fwd_kvlen",
     "dit_attn_merge",
     "dit_attn_fwd_merge",
@@ -151,6 +153,11 @@ def _declare(lib):
     lib.dit_attn_fwd.restype = ctypes.c_int
     lib.dit_attn_fwd.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                      ctypes.c_int, _P]
+    lib.dit_attn_workspace_size.restype = ctypes.c_int
+    lib.dit_attn_workspace_size.argtypes = [_I32] * 5 + [ctypes.c_int, ctypes.c_int, _I32, _I64P]
+    lib.dit_attn_fwd_ws.restype = ctypes.c_int
+    lib.dit_attn_fwd_ws.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                        ctypes.c_int, _P, ctypes.c_int64, _P]
     lib.dit_attn_fwd_kvlen.restype = ctypes.c_int
     lib.dit_attn_fwd_kvlen.argtypes = [_P, _P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                                ctypes.c_int, _I32, _P]
@@ -158,7 +165,7 @@ def _declare(lib):
     lib.dit_attn_merge.argtypes = [_P, _P, _P, _P] + [_I32] * 4 + [ctypes.c_int, _P]
     lib.dit_attn_fwd_merge.restype = ctypes.c_int
     lib.dit_attn_fwd_merge.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
-                                                                           ctypes.c_int, _P]
+                                                                           ctypes.c_int, _P, ctypes.c_int64, _P]
     lib.dit_cfg_combine.restype = ctypes.c_int
     lib.dit_cfg_combine.argtypes = [_P, _P, _P, ctypes.c_int64, ctypes.c_float, ctypes.c_int, _P]
 

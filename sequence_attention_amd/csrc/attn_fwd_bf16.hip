@@ -44,6 +44,7 @@
 //    land on the same XCD (workgroups are dealt round-robin over the 8
 //    XCDs): the head's K/V stream is then served from that XCD's L2.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "dit_internal.h"
@@ -77,7 +78,7 @@ struct Params {
   void* o;
   float* lse;
   float* part;    // partial-result slots, one per workgroup of the split round
-  int32_t* cnt;   // arrival counters of the split tiles, zero between launches
+  int32_t* cnt;   // arrival counters of the split tiles: zero on entry, left zero
   const int32_t* kv_len;  // valid keys per batch ([B], device), or null: all Skv
   int32_t Sq, Skv, H;
   int32_t n_qtiles;
@@ -549,8 +550,65 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   }
 }
 
+// How a call is laid out over the workgroups: one workgroup per tile, in
+// rounds of `slots` resident workgroups (CUs x occupancy).  When the last
+// round would leave many of them idle, its tiles are instead cut into
+// `split` key chunks, one workgroup each, merged by the online-softmax rule;
+// that needs `ws_bytes` of workspace: the arrival counters (room for one
+// per resident workgroup, padded to 256 bytes), then one partial-result
+// slot per chunk.
+struct Plan {
+  uint64_t n_tiles = 0, last = 0, split = 1;
+  size_t cnt_bytes = 0, ws_bytes = 0;
+};
+
+template <int D, bool kOutF32, bool kMerge>
+hipError_t occupancy_of(int dev, int* occ) {
+  static std::atomic<int> cached[kMaxDevices];  // per instantiation, zero-initialised
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    const hipError_t e =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<D, kOutF32, kMerge>, kThreads, 0);
+    if (e != hipSuccess) return e;
+    if (n < 1) n = 1;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  *occ = n;
+  return hipSuccess;
+}
+
+template <int D, bool kOutF32, bool kMerge>
+hipError_t plan_t(const AttnArgs& a, Plan* pl) {
+  *pl = Plan();
+  const uint64_t n_qtiles = (a.Sq + kBM - 1) / kBM;
+  const uint64_t nblocks = (a.Skv + kBN - 1) / kBN;
+  pl->n_tiles = n_qtiles * a.H * a.B;
+  if (pl->n_tiles == 0 || nblocks == 0 || a.kv_len != nullptr) return hipSuccess;  // masks: whole tiles
+  int dev = 0, occ = 0, cus = 0;
+  hipError_t e;
+  if ((e = current_device(&dev)) != hipSuccess) return e;
+  if ((e = occupancy_of<D, kOutF32, kMerge>(dev, &occ)) != hipSuccess) return e;
+  if ((e = device_cu_count(&cus)) != hipSuccess) return e;
+  const uint64_t slots = (uint64_t)cus * occ;
+  pl->last = pl->n_tiles % slots;  // tiles of the last, partial round
+  if (pl->last == 0) return hipSuccess;
+  const uint64_t split = std::min<uint64_t>({kMaxSplit, slots / pl->last, nblocks});
+  if (split < 2) return hipSuccess;
+  pl->split = split;
+  // The counter region has one fixed size for every call on the device
+  // (split tiles are fewer than `slots`), so one workspace reused by calls
+  // of different shapes never finds an earlier call's slot data where its
+  // counters must be zero.
+  pl->cnt_bytes = (slots * sizeof(int32_t) + 255) / 256 * 256;
+  pl->ws_bytes = pl->cnt_bytes + pl->last * split * slot_floats<D>() * sizeof(float);
+  return hipSuccess;
+}
+
 template <int D, bool kOutF32, bool kMerge>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
+  Plan pl;
+  hipError_t e = plan_t<D, kOutF32, kMerge>(a, &pl);
+  if (e != hipSuccess) return e;
   Params p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -562,50 +620,36 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.Skv = a.Skv;
   p.H = a.H;
   p.n_qtiles = (a.Sq + kBM - 1) / kBM;
-  const uint64_t n_tiles = (uint64_t)p.n_qtiles * a.H * a.B;
   p.nblocks = (a.Skv + kBN - 1) / kBN;
   p.scale = a.scale;
-  if (n_tiles == 0 || p.nblocks == 0) return hipSuccess;
-
-  // One workgroup per tile, in rounds of `slots` resident workgroups.  When
-  // the last round would leave many of them idle, its tiles are instead cut
-  // into `split` key chunks, one workgroup each, merged by the online-softmax
-  // rule.
-  static int occupancy[kMaxDevices] = {};  // per instantiation
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  if (occupancy[dev] == 0) {
-    int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, kOutF32, kMerge>, kThreads, 0);
-    if (e != hipSuccess) return e;
-    occupancy[dev] = per_cu > 0 ? per_cu : 1;
-  }
-  int cus = 0;
-  if ((e = device_cu_count(&cus)) != hipSuccess) return e;
-  const uint64_t slots = (uint64_t)cus * occupancy[dev];
-  const uint64_t last = n_tiles % slots;  // tiles of the last, partial round
-  uint64_t split = last == 0 ? 1 : std::min<uint64_t>({kMaxSplit, slots / last, (uint64_t)p.nblocks});
-  if (a.kv_len != nullptr) split = 1;  // per-batch lengths: whole tiles only
-  if (split < 2) split = 1;
-  p.n_whole = (uint32_t)(split > 1 ? n_tiles - last : n_tiles);
-  p.split = (uint32_t)split;
-  p.split_wgs = (uint32_t)(split > 1 ? last * split : 0);
+  if (pl.n_tiles == 0 || p.nblocks == 0) return hipSuccess;
+  // without (enough) workspace every tile is taken whole
+  const bool split = pl.split > 1 && a.workspace != nullptr && a.workspace_bytes >= pl.ws_bytes;
+  p.n_whole = (uint32_t)(split ? pl.n_tiles - pl.last : pl.n_tiles);
+  p.split = split ? (uint32_t)pl.split : 1u;
+  p.split_wgs = split ? (uint32_t)(pl.last * pl.split) : 0u;
+  p.cnt = split ? static_cast<int32_t*>(a.workspace) : nullptr;
+  p.part = split ? reinterpret_cast<float*>(static_cast<char*>(a.workspace) + pl.cnt_bytes) : nullptr;
   const uint64_t grid = (uint64_t)p.n_whole + p.split_wgs;
-
-  void* cnt = nullptr;
-  void* part = nullptr;
-  e = stream_workspace(stream, std::max<uint64_t>(last, 1) * sizeof(int32_t),
-                       std::max<uint64_t>(p.split_wgs, 1) * slot_floats<D>() * sizeof(float), &cnt, &part);
-  if (e != hipSuccess) return e;
-  p.cnt = static_cast<int32_t*>(cnt);
-  p.part = static_cast<float*>(part);
   attn_bf16_kernel<D, kOutF32, kMerge><<<(unsigned)grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
+template <int D, bool kOutF32>
+hipError_t workspace_t(const AttnArgs& a, size_t* bytes) {
+  Plan pl;
+  const hipError_t e = a.merge ? plan_t<D, kOutF32, true>(a, &pl) : plan_t<D, kOutF32, false>(a, &pl);
+  *bytes = pl.ws_bytes;
+  return e;
+}
+
 }  // namespace
+
+hipError_t attn_bf16_workspace_bytes(const AttnArgs& a, size_t* bytes) {
+  *bytes = 0;
+  if (a.D == 64) return a.o_f32 ? workspace_t<64, true>(a, bytes) : workspace_t<64, false>(a, bytes);
+  return a.o_f32 ? workspace_t<128, true>(a, bytes) : workspace_t<128, false>(a, bytes);
+}
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.merge) {

@@ -2,7 +2,8 @@
 // dispatch.  Every check runs on the host before any HIP call, so a failed
 // call writes nothing and touches no device (the CPU test suite drives every
 // error path on a machine without a GPU).  The library keeps no state apart
-// from the calling thread's last error text.
+// from the calling thread's last error text and per-device facts (compute
+// unit count, kernel occupancy) cached on first use.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -618,25 +619,68 @@ dit_status_t dit_ulysses_unpack_fp8(const dit_a2a_layout* L, dit_a2a_dir_t dir, 
 
 namespace {
 
-// dit_attn_fwd and dit_attn_fwd_merge: one validation path; `merge` makes
-// (o, lse) an accumulator that this call merges into.
-dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
-                       int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale, dit_dtype_t in_dtype,
-                       dit_dtype_t o_dtype, void* stream, bool merge, const int32_t* kv_len = nullptr,
-                       bool has_kv_len = false) {
+// Checks shared by every attention call and the workspace size query.
+dit_status_t check_attn_shape(int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D,
+                              dit_dtype_t in_dtype, dit_dtype_t o_dtype) {
   if (B < 0 || Sq < 0 || Skv < 0 || H < 0 || D < 0)
     return fail(DIT_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Skv=%d H=%d D=%d)", B, Sq, Skv,
                 H, D);
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype))
     return fail(DIT_ERR_INVALID_ARGUMENT, "unknown dtype (in=%d o=%d)", (int)in_dtype, (int)o_dtype);
-  if (!(scale > 0.0f) || !isfinite(scale))
-    return fail(DIT_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (in_dtype == DIT_F16) return fail(DIT_ERR_UNSUPPORTED, "fp16 attention is not served");
   if (in_dtype == DIT_BF16 && o_dtype != DIT_BF16 && o_dtype != DIT_F32)
     return fail(DIT_ERR_UNSUPPORTED, "bf16 attention writes bf16 or fp32 output");
   if (in_dtype == DIT_F32 && o_dtype != DIT_F32)
     return fail(DIT_ERR_UNSUPPORTED, "fp32 attention writes fp32 output");
   if (D != 64 && D != 128) return fail(DIT_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", D);
+  // tile counts are 32-bit; the fp32 path puts H and B on grid y / z
+  if ((int64_t)B * H * ((Sq + 127) / 128) >= (int64_t)1 << 31)
+    return fail(DIT_ERR_UNSUPPORTED, "too many query tiles");
+  // the bf16 kernel addresses a 64-row K/V block with 32-bit byte offsets
+  if ((int64_t)H * D * 2 * 64 >= ((int64_t)1 << 30))
+    return fail(DIT_ERR_UNSUPPORTED, "row stride H*D=%lld too large", (long long)H * D);
+  if (in_dtype == DIT_F32 && (H > 65535 || B > 65535))
+    return fail(DIT_ERR_UNSUPPORTED, "fp32 path limits B and H to 65535");
+  return DIT_OK;
+}
+
+dit::AttnArgs attn_args(int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
+                        dit_dtype_t o_dtype, bool merge) {
+  dit::AttnArgs a;
+  a.q = a.k = a.v = nullptr;
+  a.o = nullptr;
+  a.lse = nullptr;
+  a.B = B; a.Sq = Sq; a.Skv = Skv; a.H = H; a.D = D;
+  a.scale = scale;
+  a.o_f32 = (o_dtype == DIT_F32);
+  a.merge = merge;
+  return a;
+}
+
+// Workspace bytes of a validated call (0 when no tile is ever split: fp32
+// path, empty calls, per-batch key lengths).
+dit_status_t attn_workspace_need(const dit::AttnArgs& a, dit_dtype_t in_dtype, bool has_kv_len,
+                                 size_t* need) {
+  *need = 0;
+  if (in_dtype != DIT_BF16 || has_kv_len || (int64_t)a.B * a.Sq * a.H == 0 || a.Skv == 0) return DIT_OK;
+  return hip_status(dit::attn_bf16_workspace_bytes(a, need), "workspace size query");
+}
+
+// dit_attn_fwd, _ws, _kvlen and _merge: one validation path; `merge` makes
+// (o, lse) an accumulator that this call merges into.
+dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                       int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale, dit_dtype_t in_dtype,
+                       dit_dtype_t o_dtype, void* stream, bool merge, const int32_t* kv_len = nullptr,
+                       bool has_kv_len = false, void* workspace = nullptr, int64_t workspace_bytes = 0) {
+  dit_status_t st = check_attn_shape(B, Sq, Skv, H, D, in_dtype, o_dtype);
+  if (st != DIT_OK) return st;
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(DIT_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if (workspace_bytes < 0) return fail(DIT_ERR_INVALID_ARGUMENT, "workspace_bytes < 0");
+  if (workspace == nullptr && workspace_bytes != 0)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "workspace is NULL but workspace_bytes is not 0");
+  if (workspace != nullptr && !aligned(workspace, 256))
+    return fail(DIT_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   if ((int64_t)B * Sq * H == 0) {
     clear_error();
     return DIT_OK;
@@ -658,36 +702,64 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
       overlap(o, o_bytes, v, kv_bytes) ||
       (lse != nullptr && overlap(lse, (size_t)B * H * Sq * 4, o, o_bytes)))
     return fail(DIT_ERR_INVALID_ARGUMENT, "outputs overlap inputs");
-  // tile counts are 32-bit; the fp32 path puts H and B on grid y / z
-  if ((int64_t)B * H * ((Sq + 127) / 128) >= (int64_t)1 << 31)
-    return fail(DIT_ERR_UNSUPPORTED, "too many query tiles");
-  // the bf16 kernel addresses a 64-row K/V block with 32-bit byte offsets
-  if ((int64_t)H * D * 2 * 64 >= ((int64_t)1 << 30))
-    return fail(DIT_ERR_UNSUPPORTED, "row stride H*D=%lld too large", (long long)H * D);
-  if (in_dtype == DIT_F32 && (H > 65535 || B > 65535))
-    return fail(DIT_ERR_UNSUPPORTED, "fp32 path limits B and H to 65535");
+  if (workspace != nullptr) {
+    const size_t wb = (size_t)workspace_bytes;
+    if (overlap(workspace, wb, o, o_bytes) || overlap(workspace, wb, q, q_bytes) ||
+        overlap(workspace, wb, k, kv_bytes) || overlap(workspace, wb, v, kv_bytes) ||
+        (lse != nullptr && overlap(workspace, wb, lse, (size_t)B * H * Sq * 4)))
+      return fail(DIT_ERR_INVALID_ARGUMENT, "workspace overlaps a tensor");
+  }
 
   if (merge && Skv == 0) {  // an empty chunk is the merge identity
     clear_error();
     return DIT_OK;
   }
-  dit::AttnArgs a;
+  dit::AttnArgs a = attn_args(B, Sq, Skv, H, D, scale, o_dtype, merge);
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.merge = merge;
   a.kv_len = has_kv_len ? kv_len : nullptr;
-  a.B = B; a.Sq = Sq; a.Skv = Skv; a.H = H; a.D = D;
-  a.scale = scale;
-  a.o_f32 = (o_dtype == DIT_F32);
+  if (workspace != nullptr) {
+    size_t need = 0;
+    if ((st = attn_workspace_need(a, in_dtype, has_kv_len, &need)) != DIT_OK) return st;
+    if ((size_t)workspace_bytes < need)
+      return fail(DIT_ERR_INVALID_ARGUMENT,
+                  "workspace of %lld bytes; this call needs %llu (dit_attn_workspace_size)",
+                  (long long)workspace_bytes, (unsigned long long)need);
+    a.workspace = workspace;
+    a.workspace_bytes = (size_t)workspace_bytes;
+  }
   hipError_t e;
   if (Skv == 0) e = dit::launch_attn_empty(a, in_dtype == DIT_F32, (hipStream_t)stream);
   else if (in_dtype == DIT_BF16) e = dit::launch_attn_fwd_bf16(a, (hipStream_t)stream);
   else e = dit::launch_attn_fwd_f32(a, (hipStream_t)stream);
-  const dit_status_t st = hip_status(e, "attention launch");
+  st = hip_status(e, "attention launch");
   if (st == DIT_OK) clear_error();
   return st;
 }
 
 }  // namespace
+
+dit_status_t dit_attn_workspace_size(int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D,
+                                     dit_dtype_t in_dtype, dit_dtype_t o_dtype, int32_t merge,
+                                     int64_t* bytes) {
+  if (bytes == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (merge != 0 && merge != 1) return fail(DIT_ERR_INVALID_ARGUMENT, "merge must be 0 or 1");
+  dit_status_t st = check_attn_shape(B, Sq, Skv, H, D, in_dtype, o_dtype);
+  if (st != DIT_OK) return st;
+  size_t need = 0;
+  st = attn_workspace_need(attn_args(B, Sq, Skv, H, D, 1.0f, o_dtype, merge == 1), in_dtype, false, &need);
+  if (st != DIT_OK) return st;
+  *bytes = (int64_t)need;
+  clear_error();
+  return DIT_OK;
+}
+
+dit_status_t dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
+                             dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  return attn_call(q, k, v, o, lse, B, Sq, Skv, H, D, scale, in_dtype, o_dtype, stream, false, nullptr,
+                   false, workspace, workspace_bytes);
+}
 
 dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                           int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
@@ -707,8 +779,9 @@ dit_status_t dit_attn_fwd_kvlen(const void* q, const void* k, const void* v, con
 dit_status_t dit_attn_fwd_merge(const void* q, const void* k, const void* v, void* o_acc,
                                 float* lse_acc, int32_t B, int32_t Sq, int32_t Skv, int32_t H,
                                 int32_t D, float scale, dit_dtype_t in_dtype, dit_dtype_t acc_dtype,
-                                void* stream) {
-  return attn_call(q, k, v, o_acc, lse_acc, B, Sq, Skv, H, D, scale, in_dtype, acc_dtype, stream, true);
+                                void* workspace, int64_t workspace_bytes, void* stream) {
+  return attn_call(q, k, v, o_acc, lse_acc, B, Sq, Skv, H, D, scale, in_dtype, acc_dtype, stream, true,
+                   nullptr, false, workspace, workspace_bytes);
 }
 
 dit_status_t dit_attn_merge(void* o_acc, float* lse_acc, const void* o_part, const float* lse_part,

@@ -34,17 +34,11 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 // ---- device resources ---------------------------------------------------------
 constexpr int kMaxDevices = 64;
 
+// The current device's index, checked against kMaxDevices.
+hipError_t current_device(int* dev);
+
 // Compute units of the current device (queried once per device).
 hipError_t device_cu_count(int* cus);
-
-// Device memory private to (current device, stream), allocated on first use
-// and grown on demand, kept until the process ends: `zeroed_bytes` of
-// memory that is all-zero when handed out (a fresh allocation is zero-filled
-// on `stream`; kernels that use it must leave it zero again) and
-// `scratch_bytes` of scratch with undefined contents.  Growth first waits for
-// the stream's earlier work, which may still use the old allocation.
-hipError_t stream_workspace(hipStream_t stream, size_t zeroed_bytes, size_t scratch_bytes,
-                            void** zeroed, void** scratch);
 
 // ---- Ulysses permutes -------------------------------------------------------
 enum PermuteKind : int {
@@ -138,8 +132,16 @@ struct AttnArgs {
   bool o_f32;  // bf16 input only: write O as fp32
   bool merge = false;  // o / lse hold a partial result to merge this call into
   const int32_t* kv_len = nullptr;  // [B] valid keys per batch (device), or null
+  // Caller-owned device memory for the split last round of the bf16 path
+  // (arrival counters, all zero on entry and left zero, then partial-result
+  // slots), or null: tiles are then never split.
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
 };
 
+// Bytes of workspace the bf16 path uses for this call on the current device
+// (0: no tile is split).  Host-only queries of the device.
+hipError_t attn_bf16_workspace_bytes(const AttnArgs& a, size_t* bytes);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
 // Skv == 0: O = 0, LSE = -inf.

@@ -55,7 +55,7 @@ def test_header_is_plain_c():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dit_abi_version() == 1
+    assert lib.dit_abi_version() == 2
     for code, name in [(0, "DIT_OK"), (1, "DIT_ERR_INVALID_ARGUMENT"), (2, "DIT_ERR_UNSUPPORTED"),
                        (3, "DIT_ERR_HIP")]:
         assert lib.dit_status_string(code).decode() == name
@@ -194,9 +194,9 @@ def test_attn_empty_is_a_no_op(lib):
 
 
 def _attn_merge(lib, q=A, k=A + 2**24, v=A + 2**25, o=A + 2**26, lse=A + 2**27, B=1, Sq=128, Skv=128,
-                H=2, D=64, scale=0.125, din=0, dacc=0):
+                H=2, D=64, scale=0.125, din=0, dacc=0, ws=0, ws_bytes=0):
     return lib.dit_attn_fwd_merge(P(q), P(k), P(v), P(o), P(lse), B, Sq, Skv, H, D, scale, din, dacc,
-                                  NULL)
+                                  P(ws), ws_bytes, NULL)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -210,6 +210,60 @@ def _attn_merge(lib, q=A, k=A + 2**24, v=A + 2**25, o=A + 2**26, lse=A + 2**27, 
 def test_attn_fwd_merge_rejects(lib, kw, code):
     assert _attn_merge(lib, **kw) == code, lib.dit_last_error()
     assert lib.dit_last_error().decode() != ""
+
+
+def _attn_ws(lib, q=A, k=A + 2**24, v=A + 2**25, o=A + 2**26, lse=A + 2**27, B=1, Sq=128, Skv=128,
+             H=2, D=64, scale=0.125, din=0, dout=0, ws=A + 2**29, ws_bytes=1 << 20):
+    return lib.dit_attn_fwd_ws(P(q), P(k), P(v), P(o), P(lse), B, Sq, Skv, H, D, scale, din, dout,
+                               P(ws), ws_bytes, NULL)
+
+
+# workspace arguments are checked before any device query or launch
+@pytest.mark.parametrize("call", ["ws", "merge"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=0, ws_bytes=64), INV),                 # NULL workspace with a size
+    (dict(ws_bytes=-1), INV),                       # negative size
+    (dict(ws=A + 2**29 + 16), UNS),                 # not 256-byte aligned
+    (dict(ws=A + 2**26, ws_bytes=1 << 20), INV),    # workspace overlaps o
+    (dict(ws=A, ws_bytes=1 << 20), INV),            # workspace overlaps q
+    (dict(B=-1), INV), (dict(D=96), UNS), (dict(scale=0.0), INV),
+])
+def test_attn_workspace_rejects(lib, call, kw, code):
+    if call == "ws":
+        st = _attn_ws(lib, **kw)
+    else:
+        kw = {k2: v2 for k2, v2 in kw.items()}
+        kw.setdefault("ws", A + 2**29)
+        kw.setdefault("ws_bytes", 1 << 20)
+        st = _attn_merge(lib, **kw)
+    assert st == code, lib.dit_last_error()
+    assert lib.dit_last_error().decode() != ""
+
+
+def test_attn_ws_empty_is_a_no_op(lib):
+    assert _attn_ws(lib, q=0, k=0, v=0, o=0, lse=0, Sq=0) == 0
+    assert _attn_ws(lib, ws=0, ws_bytes=0, q=0, k=0, v=0, o=0, lse=0, B=0) == 0
+
+
+def _ws_size(lib, B=1, Sq=128, Skv=128, H=2, D=64, din=0, dout=0, merge=0, out=True):
+    n = ctypes.c_int64(-5)
+    st = lib.dit_attn_workspace_size(B, Sq, Skv, H, D, din, dout, merge, ctypes.byref(n) if out else None)
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=False), INV), (dict(merge=2), INV), (dict(B=-1), INV), (dict(din=9), INV),
+    (dict(D=96), UNS), (dict(din=1, dout=1), UNS), (dict(din=2, dout=0), UNS),
+])
+def test_attn_workspace_size_rejects(lib, kw, code):
+    assert _ws_size(lib, **kw)[0] == code, lib.dit_last_error()
+
+
+def test_attn_workspace_size_without_a_device_query(lib):
+    # calls that never split need no workspace and touch no device
+    assert _ws_size(lib, din=2, dout=2) == (0, 0)          # fp32 path
+    assert _ws_size(lib, Sq=0) == (0, 0)
+    assert _ws_size(lib, Skv=0, merge=1) == (0, 0)
 
 
 def test_attn_fwd_merge_empty_chunk_is_a_no_op(lib):

@@ -225,7 +225,7 @@ def test_custom_scale():
 # Shapes whose last round of tiles is cut into key chunks merged by the
 # last-arriving chunk (on a 256-CU device: 8, 8, 3 and 4 chunks per tile;
 # the fourth mixes tiles taken whole with split ones), run back to back so
-# that the per-stream workspace is reused across different tile counts.
+# that one workspace is reused across different tile counts.
 SPLIT_SEQUENCE = [
     # B, Sq, Skv, H, D
     (1, 1000, 1000, 8, 128),   # 32 tiles, all split
@@ -237,13 +237,37 @@ SPLIT_SEQUENCE = [
 
 
 def test_split_tiles_and_workspace_reuse():
+    # one explicit caller workspace, sized for the largest call and zeroed
+    # once, shared by every call of the sequence (the kernels leave its
+    # counters zero); the no-workspace entry point takes every tile whole
+    sizes = [sa.dit_attn_workspace_size(B, Sq, Skv, H, D) for B, Sq, Skv, H, D in SPLIT_SEQUENCE]
+    assert all(n > 0 for n in sizes)
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=DEV)
     for i, shape in enumerate(SPLIT_SEQUENCE):
         B, Sq, Skv, H, D = shape
         log(f"attn bf16 split-tile sequence {i} {shape}")
         w = workloads.Workload("split", B=B, Sq=Sq, Skv=Skv, H=H, D=D, R=1, S=Skv, H_total=H, U=1)
         q, k, v = workloads.attention_inputs(w, seed=100 + i)
-        o, lse = run_attn(q, k, v, w.scale)
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        o, lse = sa.dit_attn_fwd_ws(qd, kd, vd, ws, scale=w.scale)
+        o2, lse2 = sa.dit_attn_fwd(qd, kd, vd, scale=w.scale, workspace=False)
+        torch.cuda.synchronize()
         check(o, lse, q, k, v, w.scale, what=f"split {shape}")
+        check(o2, lse2, q, k, v, w.scale, what=f"whole tiles {shape}")
+    assert torch.count_nonzero(ws[:1024]).item() == 0   # counters left zero
+
+
+def test_workspace_smaller_than_needed_is_rejected():
+    B, Sq, Skv, H, D = SPLIT_SEQUENCE[0]
+    need = sa.dit_attn_workspace_size(B, Sq, Skv, H, D)
+    q = torch.zeros((B, Sq, H, D), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((B, Skv, H, D), dtype=torch.bfloat16, device=DEV)
+    small = torch.zeros(need - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(sa.DitError) as e:
+        sa.dit_attn_fwd_ws(q, kv, kv, small)
+    assert e.value.status == sa.DIT_ERR_INVALID_ARGUMENT and "needs" in e.value.detail
+    # shapes that fill the device's rounds exactly need none
+    assert sa.dit_attn_workspace_size(1, 256 * 256, 512, 1, 128) == 0
 
 
 def test_side_stream_matches_default_stream():
