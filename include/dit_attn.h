@@ -385,8 +385,9 @@ dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, 
  * device's compute-unit count decides how the work is cut).  0 means the
  * call never splits a tile (fp32 path, empty calls, shapes that fill the
  * device's rounds exactly).  Arguments as dit_attn_fwd.  For a bf16 call on a
- * 256-CU device the size is at most 256 x 139264 + 1024 bytes (about
- * 35.7 MB at D = 128).  Host-only apart from device attribute queries.
+ * 256-CU device the size is at most 65536 + 256 x 139264 bytes (about
+ * 35.7 MB at D = 128).  Layout: 65536 bytes of arrival counters (the same
+ * for every call), then the partial-result slots.  Host-only apart from device attribute queries.
  * Errors: INVALID_ARGUMENT (bytes NULL, negative size, bad dtype or merge),
  * UNSUPPORTED (as dit_attn_fwd), HIP (no device).
  */
@@ -404,9 +405,9 @@ dit_status_t dit_attn_workspace_size(int32_t B, int32_t Sq, int32_t Skv, int32_t
  * attention tolerance (not bitwise: the split changes the summation order).
  *
  * workspace: device memory of workspace_bytes bytes, 256-byte aligned,
- *   whose first bytes (the arrival counters) are ZERO the first time it is
- *   used (e.g. zero-filled once after allocation); every call leaves them
- *   zero again.  NULL with workspace_bytes = 0: no split (= dit_attn_fwd).
+ *   whose first 65536 bytes (the arrival counters) are ZERO the first time
+ *   it is used (e.g. zero-filled once after allocation); every call leaves
+ *   them zero again, so one workspace serves calls of any shape.  NULL with workspace_bytes = 0: no split (= dit_attn_fwd).
  *   workspace_bytes must be at least dit_attn_workspace_size() for the call.
  *   Calls that may run at the same time (different streams) need different
  *   workspaces; calls on one stream may share one.

@@ -554,9 +554,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
 // rounds of `slots` resident workgroups (CUs x occupancy).  When the last
 // round would leave many of them idle, its tiles are instead cut into
 // `split` key chunks, one workgroup each, merged by the online-softmax rule;
-// that needs `ws_bytes` of workspace: the arrival counters (room for one
-// per resident workgroup, padded to 256 bytes), then one partial-result
-// slot per chunk.
+// that needs `ws_bytes` of workspace: a fixed region of arrival counters
+// (kAttnCounterBytes), then one partial-result slot per chunk.
 struct Plan {
   uint64_t n_tiles = 0, last = 0, split = 1;
   size_t cnt_bytes = 0, ws_bytes = 0;
@@ -595,11 +594,12 @@ hipError_t plan_t(const AttnArgs& a, Plan* pl) {
   const uint64_t split = std::min<uint64_t>({kMaxSplit, slots / pl->last, nblocks});
   if (split < 2) return hipSuccess;
   pl->split = split;
-  // The counter region has one fixed size for every call on the device
-  // (split tiles are fewer than `slots`), so one workspace reused by calls
-  // of different shapes never finds an earlier call's slot data where its
-  // counters must be zero.
-  pl->cnt_bytes = (slots * sizeof(int32_t) + 255) / 256 * 256;
+  // The counter region has one fixed size for every call (split tiles are
+  // fewer than `slots`), so a workspace reused by calls of different shapes
+  // or kernels never finds an earlier call's slot data where its counters
+  // must be zero.
+  if (pl->last * sizeof(int32_t) > kAttnCounterBytes) return hipErrorInvalidConfiguration;
+  pl->cnt_bytes = kAttnCounterBytes;
   pl->ws_bytes = pl->cnt_bytes + pl->last * split * slot_floats<D>() * sizeof(float);
   return hipSuccess;
 }

@@ -142,6 +142,10 @@ struct AttnArgs {
 // Bytes of workspace the bf16 path uses for this call on the current device
 // (0: no tile is split).  Host-only queries of the device.
 hipError_t attn_bf16_workspace_bytes(const AttnArgs& a, size_t* bytes);
+// Workspace layout of the split last round: a fixed region of arrival
+// counters (room for 16384 split tiles; one size for every call, so calls of
+// different shapes may share a workspace), then partial-result slots.
+constexpr size_t kAttnCounterBytes = size_t(64) << 10;
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
 // Skv == 0: O = 0, LSE = -inf.
