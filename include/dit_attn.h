@@ -19,6 +19,8 @@
  *                                          with a caller workspace that lets
  *                                          the kernel split the last round)
  *   dit_attn_workspace_size                that workspace's size
+ *   dit_attn_fwd_noalloc                   ... with a static scratch instead
+ *                                          (callers that cannot allocate)
  *   dit_attn_fwd_kvlen                     ... over a per-batch key prefix
  *   dit_attn_merge                         online-softmax merge of partial
  *                                          results (ring hops)
@@ -419,6 +421,27 @@ dit_status_t dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* 
                              int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
                              dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* workspace,
                              int64_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dit_attn_fwd_ws with the workspace taken from a static scratch array in
+ * the library instead of an argument.  Arguments and results as
+ * dit_attn_fwd_ws; no call allocates.
+ *
+ * The scratch is one 36 MiB (37748736-byte) array per device, held from the
+ * first call on that device until the process ends; its counter region is
+ * zeroed by the first call on the device (on that call's stream) and left
+ * zero by every call.  Every call on a device shares it, so calls that may
+ * overlap on one device (different streams, or threads without ordering)
+ * RACE: serialize them.  A call whose split plan needs more than the scratch
+ * holds is refused (DIT_ERR_UNSUPPORTED) before anything runs; on a 256-CU
+ * device no call does (at most 65536 + 256 x 139264 bytes).
+ * Errors: as dit_attn_fwd; UNSUPPORTED also for a plan beyond the scratch.
+ */
+dit_status_t dit_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
+                                  dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* stream);
 
 /*
  * Attention over a per-batch prefix of the keys: keys j >= kv_len[b] of

@@ -33,7 +33,7 @@ __all__ = [
     "dit_ulysses_unpack_uneven", "dit_ring_anything_pad", "dit_ring_anything_trim",
     "DitA2AUnevenLayout",
     "dit_a2a_fp8_bytes_per_peer", "dit_ulysses_pack_fp8", "dit_ulysses_unpack_fp8",
-    "dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_workspace_size", "dit_attn_fwd_kvlen", "dit_attn_merge",
+    "dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_noalloc", "dit_attn_workspace_size", "dit_attn_fwd_kvlen", "dit_attn_merge",
     "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
@@ -456,6 +456,21 @@ def dit_attn_fwd_ws(q, k, v, workspace, o=None, lse=None, scale=None, o_dtype=No
         raise ValueError("workspace must be a uint8 tensor")
     return dit_attn_fwd(q, k, v, o=o, lse=lse, scale=scale, o_dtype=o_dtype, stream=stream,
                         workspace=workspace)
+
+
+def dit_attn_fwd_noalloc(q, k, v, o, lse, scale=None, stream=None):
+    """dit_attn_fwd with the library's static scratch as workspace: o and
+    lse are caller buffers, nothing is allocated.  Calls that may overlap on
+    one device race on the shared scratch."""
+    B, Sq, Skv, H, D = _check_qkv(q, k, v)
+    _check_out(o, lse, B, Sq, H, D, q.device, False)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lse_ptr = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
+    check(lib().dit_attn_fwd_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lse_ptr,
+                                     B, Sq, Skv, H, D, float(scale), _dtype_code(q.dtype),
+                                     _dtype_code(o.dtype), _stream(stream)), "dit_attn_fwd_noalloc")
+    return o, lse
 
 
 def dit_attn_fwd_kvlen(q, k, v, kv_len, o=None, lse=None, scale=None, o_dtype=None, merge=False,

@@ -46,6 +46,7 @@ EXPORTS = (
     "dit_attn_fwd",
     "dit_attn_workspace_size",
     "dit_attn_fwd_ws",
+    "dit_attn_fwd_noalloc",
     "dit_attn_fwd_kvlen",
     "dit_attn_merge",
     "dit_attn_fwd_merge",
@@ -158,6 +159,9 @@ def _declare(lib):
     lib.dit_attn_fwd_ws.restype = ctypes.c_int
     lib.dit_attn_fwd_ws.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                         ctypes.c_int, _P, ctypes.c_int64, _P]
+    lib.dit_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.dit_attn_fwd_noalloc.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                            ctypes.c_int, _P]
     lib.dit_attn_fwd_kvlen.restype = ctypes.c_int
     lib.dit_attn_fwd_kvlen.argtypes = [_P, _P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                                ctypes.c_int, _I32, _P]

@@ -45,6 +45,7 @@
 //    XCDs): the head's K/V stream is then served from that XCD's L2.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "dit_internal.h"
@@ -643,7 +644,56 @@ hipError_t workspace_t(const AttnArgs& a, size_t* bytes) {
   return e;
 }
 
+// ---- scratch of the no-allocation entry point ----------------------------------
+// A file-scope device array stands in for the caller's workspace: the
+// counter region plus 256 partial-result slots at D = 128 (the most a
+// 256-CU device's split round uses) fit in kAttnScratchBytes = 36 MiB.  Each
+// device that runs the library holds its own copy until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is
+// only a stand-in): it uses the address hipGetSymbolAddress returns for the
+// current device.
+__device__ __align__(256) char scratch[kAttnScratchBytes];
+static_assert(kAttnScratchBytes >= kAttnCounterBytes + 256 * slot_floats<128>() * sizeof(float),
+              "scratch holds a 256-CU device's split round");
+
+__global__ void zero_words(uint32_t* p, uint32_t n) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+struct ScratchState {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchState g_scratch[kMaxDevices];
+
 }  // namespace
+
+hipError_t attn_scratch(hipStream_t stream, void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = current_device(&dev);
+  if (e != hipSuccess) return e;
+  ScratchState& st = g_scratch[dev];
+  std::call_once(st.once, [&] {
+    void* p = nullptr;
+    st.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (st.err != hipSuccess) return;
+    // The counters must start at zero (every call leaves them zero): clear
+    // the largest counter region a call can use once, on the first caller's
+    // stream, with a kernel (not a memset node, so a caller may capture
+    // later calls in a graph).
+    constexpr uint32_t kWords = kAttnCounterBytes / 4;
+    zero_words<<<kWords / 256, 256, 0, stream>>>(static_cast<uint32_t*>(p), kWords);
+    st.err = hipGetLastError();
+    if (st.err == hipSuccess) st.ptr = p;
+  });
+  if (st.err != hipSuccess) return st.err;
+  *ptr = st.ptr;
+  *bytes = kAttnScratchBytes;
+  return hipSuccess;
+}
+
 
 hipError_t attn_bf16_workspace_bytes(const AttnArgs& a, size_t* bytes) {
   *bytes = 0;

@@ -671,7 +671,8 @@ dit_status_t attn_workspace_need(const dit::AttnArgs& a, dit_dtype_t in_dtype, b
 dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
                        int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale, dit_dtype_t in_dtype,
                        dit_dtype_t o_dtype, void* stream, bool merge, const int32_t* kv_len = nullptr,
-                       bool has_kv_len = false, void* workspace = nullptr, int64_t workspace_bytes = 0) {
+                       bool has_kv_len = false, void* workspace = nullptr, int64_t workspace_bytes = 0,
+                       bool static_scratch = false) {
   dit_status_t st = check_attn_shape(B, Sq, Skv, H, D, in_dtype, o_dtype);
   if (st != DIT_OK) return st;
   if (!(scale > 0.0f) || !isfinite(scale))
@@ -726,6 +727,20 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
                   (long long)workspace_bytes, (unsigned long long)need);
     a.workspace = workspace;
     a.workspace_bytes = (size_t)workspace_bytes;
+  } else if (static_scratch) {
+    size_t need = 0;
+    if ((st = attn_workspace_need(a, in_dtype, has_kv_len, &need)) != DIT_OK) return st;
+    if (need > dit::kAttnScratchBytes)
+      return fail(DIT_ERR_UNSUPPORTED, "this call needs %llu bytes of scratch; the static scratch holds %llu",
+                  (unsigned long long)need, (unsigned long long)dit::kAttnScratchBytes);
+    if (need > 0) {
+      void* ptr = nullptr;
+      size_t cap = 0;
+      if ((st = hip_status(dit::attn_scratch((hipStream_t)stream, &ptr, &cap), "static scratch")) != DIT_OK)
+        return st;
+      a.workspace = ptr;
+      a.workspace_bytes = cap;
+    }
   }
   hipError_t e;
   if (Skv == 0) e = dit::launch_attn_empty(a, in_dtype == DIT_F32, (hipStream_t)stream);
@@ -759,6 +774,13 @@ dit_status_t dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* 
                              int64_t workspace_bytes, void* stream) {
   return attn_call(q, k, v, o, lse, B, Sq, Skv, H, D, scale, in_dtype, o_dtype, stream, false, nullptr,
                    false, workspace, workspace_bytes);
+}
+
+dit_status_t dit_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
+                                  dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* stream) {
+  return attn_call(q, k, v, o, lse, B, Sq, Skv, H, D, scale, in_dtype, o_dtype, stream, false, nullptr,
+                   false, nullptr, 0, true);
 }
 
 dit_status_t dit_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

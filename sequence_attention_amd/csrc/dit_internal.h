@@ -146,6 +146,12 @@ hipError_t attn_bf16_workspace_bytes(const AttnArgs& a, size_t* bytes);
 // counters (room for 16384 split tiles; one size for every call, so calls of
 // different shapes may share a workspace), then partial-result slots.
 constexpr size_t kAttnCounterBytes = size_t(64) << 10;
+// Size of the static scratch of the no-allocation entry point.
+constexpr size_t kAttnScratchBytes = size_t(36) << 20;
+// The current device's static scratch (address and size) for callers that
+// cannot allocate; its counter region is zeroed on the first call per device
+// (on `stream`).  Every call on a device shares it.
+hipError_t attn_scratch(hipStream_t stream, void** ptr, size_t* bytes);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
 // Skv == 0: O = 0, LSE = -inf.
