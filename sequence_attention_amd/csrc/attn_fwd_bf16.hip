@@ -30,9 +30,12 @@
 //    read: a 16-lane group gets a 4-key x 16-dim block with one dim per
 //    lane), in the key order the accumulator reuse implies.
 //  * Softmax runs in fp32 with exp2 and scale*log2(e) folded into one FMA.
-//    The running max is only raised when a block's max exceeds it by more
-//    than 2^8 in the exp2 domain (a wave-uniform branch), so the O rescale
-//    is rare; P then stays <= 256, far from fp32 limits.  The PV product
+//    The weights are taken against a running reference score that is
+//    raised only when some weight of a block would exceed 2^32 (a
+//    wave-uniform test on the lanes' block sums, which also catches the
+//    first block): no per-block row max is computed, and the O rescale is
+//    rare.  Weights up to 2^32 keep fp32 sums and accumulators far from
+//    overflow, and bf16 keeps 8 significant bits at any magnitude.  The PV product
 //    uses P rounded to bf16, so O is normalised by the sum of those rounded
 //    weights (a consistent weighted average of V rows): with the lazy
 //    rescale the dominant weight of a near one-hot row is not exactly 1, and
@@ -67,7 +70,7 @@ constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per block
 constexpr int kNumXcd = 8;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (exp2 domain)
+constexpr float kMaxWeight = 4294967296.0f;  // 2^32: largest block weight sum per lane against the reference
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9 family)
 constexpr uint64_t kMaxSplit = 8;        // key chunks per tile in the split round
 constexpr int kScopeAgent = 16;           // buffer cache policy: sc1, device-scope coherent
@@ -309,19 +312,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
             if (key >= skv) s[t][r] = -INFINITY;
           }
       }
-      float mx = s[0][0];
+      // Weights against the running reference m_used, and this block's sums
+      // of the unrounded (bs, for LSE) and bf16-rounded (br, for O) weights.
+      bf16x8 pb[2][2];
+      float bs, br;
+      auto weights = [&]() __attribute__((always_inline)) {
+        const float mc = m_used * c;
+        bs = 0.0f;
+        br = 0.0f;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      {
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r + 1], c, -mc));
+            bs += p0;
+            bs += p1;
+            const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
+            pb[t][r >> 3][r & 7] = pr[0];
+            pb[t][r >> 3][(r & 7) + 1] = pr[1];
+            br = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, br, false);
+          }
+      };
+      weights();
+      // The reference only has to keep every weight at most 2^32 (fp32 sums
+      // and the O accumulators stay far from overflow; bf16 keeps 8 bits
+      // of any magnitude), so no row max is taken in the common case.  A
+      // lane sum above 2^32 (or NaN: the first block, with m_used = -inf,
+      // gives inf or NaN) raises the reference to the block's row max,
+      // rescales what was accumulated and recomputes the weights.
+      if (__builtin_expect(__any(!(bs <= kMaxWeight)), 0)) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      const bool raise = (mx - m_used) * c > kRescaleLog2;
-      if (__any(raise)) {
-        const float m_new = raise ? mx : m_used;
-        const float alpha = __builtin_amdgcn_exp2f((m_used - m_new) * c);
+        // a processed block always holds a valid key, so mx is finite
+        const float m_new = fmaxf(m_used, mx);
+        const float alpha = m_used == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_used - m_new) * c);
         lsum *= alpha;
         lsum_r *= alpha;
 #pragma unroll
@@ -329,33 +360,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
         m_used = m_new;
+        weights();
       }
-      const float mc = m_used * c;
-
-      // LSE needs the row sum of the unrounded P: a bf16-rounded sum would be
-      // off by up to 2^-9 relative (about 2e-3 in LSE) on near one-hot rows.
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -mc));
-          lsum += pr;
-          pb[t][r >> 3][r & 7] = (__bf16)pr;
-        }
-      {
-        // sum of the rounded weights, two per v_dot2 with (1, 1)
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const bf16x2 pair = {pb[t][hh][e], pb[t][hh][e + 1]};
-              lsum_r = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lsum_r, false);
-            }
-      }
+      lsum += bs;
+      lsum_r += br;
 
       // O^T += V^T P^T: 4 key steps of 16 keys
 #pragma unroll
