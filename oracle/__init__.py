@@ -32,6 +32,10 @@ Sources (cited by page title and section):
   execution", Ulysses section) -- the RoPE convention is not on the pages;
   the RoFormer rotation of adjacent dims with caller-given cos / sin tables
   is the reading taken (see ``reference.rope``).
+* The optional F32 -> F16 conversion of the packed QKV operator and the
+  direct F16 / BF16 output of the head-to-sequence path (edge-dit.cpp
+  "Parallel execution") -- rounding to nearest, ties to even, is the reading
+  (see ``reference.round_to_half``).
 
 Modules:
   oracle.reference  -- vectorised numpy fp64 definitions (the oracle proper)
@@ -82,4 +86,10 @@ from .reference import (  # noqa: F401
     cfg_combine,
     cfg_combine_f32,
     fmaf,
+    HALF_FORMATS,
+    half_value,
+    half_is_nan,
+    round_to_half,
+    pack_seq_to_head_convert,
+    pack_head_to_seq_convert,
 )

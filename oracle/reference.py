@@ -693,3 +693,90 @@ def cfg_combine_f32(u, c, g: float):
     c = np.asarray(c, dtype=np.float32)
     d = (c - u).astype(np.float32)
     return fmaf(np.float32(g), d, u)
+
+
+# ---------------------------------------------------------------------------
+# Packing with a conversion to a 16-bit exchange type
+# ---------------------------------------------------------------------------
+#
+# edge-dit.cpp "Parallel execution": the packed QKV operator may convert F32
+# input to F16 on the way into the send buffer, and the head-to-sequence
+# path may produce F16 or BF16 output directly.  Readings: the conversion is
+# IEEE 754 rounding to nearest with ties to even, overflow going to
+# infinity, subnormal results kept (no flush to zero), NaN staying NaN (its
+# sign and payload unspecified); BF16 is served as well as F16; pad
+# positions of the send buffer are +0.
+#
+# The formats, from their definitions (sign, biased exponent, fraction):
+#   F16  -- 1 + 5 + 10 bits, bias 15:  codes 0x7C00 inf, 0x7C01.. NaN
+#   BF16 -- 1 + 8 +  7 bits, bias 127: codes 0x7F80 inf, 0x7F81.. NaN
+
+HALF_FORMATS = {"f16": (5, 10), "bf16": (8, 7)}   # exponent bits, fraction bits
+
+
+def half_value(code, fmt):
+    """float64 value of 16-bit codes of format ``fmt`` ("f16" or "bf16")."""
+    e_bits, f_bits = HALF_FORMATS[fmt]
+    c = np.asarray(code).astype(np.int64) & 0xFFFF
+    bias = (1 << (e_bits - 1)) - 1
+    e_all = (1 << e_bits) - 1
+    sign = np.where(c >> 15, -1.0, 1.0)
+    e = (c >> f_bits) & e_all
+    f = (c & ((1 << f_bits) - 1)).astype(np.float64)
+    mag = np.where(e == 0, f * 2.0 ** (1 - bias - f_bits),
+                   (1.0 + f * 2.0 ** -f_bits) * 2.0 ** (e.astype(np.float64) - bias))
+    mag = np.where(e == e_all, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def _half_ladder(fmt):
+    """Values of the non-negative codes 0 .. inf, increasing with the code;
+    the infinity code stands at the value the next binade would start at, so
+    that overflow follows the same nearest / ties-to-even rule."""
+    e_bits, f_bits = HALF_FORMATS[fmt]
+    inf_code = ((1 << e_bits) - 1) << f_bits
+    v = half_value(np.arange(inf_code + 1), fmt)
+    bias = (1 << (e_bits - 1)) - 1
+    v[inf_code] = 2.0 ** (bias + 1)
+    return v, inf_code
+
+
+def round_to_half(x, fmt):
+    """uint16 codes of float64 values in format ``fmt``: the nearest code,
+    ties to the code whose last fraction bit is 0; magnitudes at or past the
+    midpoint between the largest finite value and 2^(emax+1) give infinity;
+    NaN gives the quiet NaN with only the top fraction bit set."""
+    ladder, inf_code = _half_ladder(fmt)
+    _, f_bits = HALF_FORMATS[fmt]
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, a)
+    hi = np.clip(np.searchsorted(ladder, a, side="left"), 0, inf_code)   # first value >= a
+    lo = np.clip(hi - 1, 0, inf_code)
+    d_hi = ladder[hi] - a
+    d_lo = a - ladder[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi)
+    code = np.where(np.isinf(a), inf_code, code)
+    code = np.where(np.signbit(x), code | 0x8000, code)
+    code = np.where(nan, inf_code | (1 << (f_bits - 1)), code)
+    return code.astype(np.uint16)
+
+
+def half_is_nan(code, fmt):
+    e_bits, f_bits = HALF_FORMATS[fmt]
+    c = np.asarray(code).astype(np.int64) & 0x7FFF
+    return c > (((1 << e_bits) - 1) << f_bits)
+
+
+def pack_seq_to_head_convert(in_planes, L, rank, fmt):
+    """The sequence-to-head send buffer of ``pack_seq_to_head`` over float32
+    planes, each element rounded to ``fmt`` (uint16 codes; pad elements +0)."""
+    return round_to_half(pack_seq_to_head(in_planes, L, rank), fmt)
+
+
+def pack_head_to_seq_convert(in_planes, L, rank, fmt):
+    """The head-to-sequence send buffer of ``pack_head_to_seq`` over float32
+    planes, each element rounded to ``fmt`` (uint16 codes; pad elements +0)."""
+    return round_to_half(pack_head_to_seq(in_planes, L, rank), fmt)
