@@ -6,6 +6,8 @@
  * call:
  *   dit_ulysses_pack / dit_ulysses_unpack  layout transforms around the
  *                                          Ulysses all-to-alls
+ *   dit_ulysses_pack_convert               the pack from float32 planes into a
+ *                                          bf16 / f16 send buffer
  *   dit_ulysses_unpack_rope                the receive-side unpack fused with
  *                                          RoPE on Q and K
  *   dit_ulysses_pack_uneven / _unpack_uneven  the same transforms for
@@ -152,6 +154,26 @@ dit_status_t dit_a2a_layout_init(int32_t B, int32_t S, int32_t H, int32_t D, int
  */
 dit_status_t dit_ulysses_pack(const dit_a2a_layout* layout, dit_a2a_dir_t dir, int32_t rank,
                               const void* const* in_planes, void* send_buf, void* stream);
+
+/*
+ * dit_ulysses_pack with float32 planes and a 16-bit send buffer: every
+ * element is rounded to layout->dtype (DIT_BF16 or DIT_F16) on its way into
+ * the buffer (edge-dit.cpp "Parallel execution": the packed QKV operator's
+ * optional F32-to-F16 conversion; F16 / BF16 output produced directly on the
+ * head-to-sequence path).  The maps, pads and buffer layout are those of
+ * dit_ulysses_pack for the same layout and direction; only the element type
+ * of in_planes differs (float32, 4-byte aligned).
+ *
+ * Rounding: IEEE 754 round to nearest, ties to even; magnitudes at or past
+ * the overflow midpoint become infinity; subnormal results are kept; NaN
+ * becomes a quiet NaN (sign and payload unspecified).  Pad elements are +0.
+ *
+ * Errors: as dit_ulysses_pack, plus UNSUPPORTED when layout->dtype is not
+ * DIT_BF16 or DIT_F16.  Uses no memory beyond its arguments.
+ */
+dit_status_t dit_ulysses_pack_convert(const dit_a2a_layout* layout, dit_a2a_dir_t dir,
+                                      int32_t rank, const void* const* in_planes, void* send_buf,
+                                      void* stream);
 
 /*
  * Unpack the receive buffer of Ulysses rank `rank` after the all-to-all

@@ -27,7 +27,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "dit_abi_version", "dit_a2a_layout_init", "dit_ulysses_pack", "dit_ulysses_unpack",
+    "dit_abi_version", "dit_a2a_layout_init", "dit_ulysses_pack", "dit_ulysses_pack_convert",
+    "dit_ulysses_unpack",
     "dit_ulysses_unpack_rope",
     "dit_a2a_uneven_init", "dit_a2a_uneven_sizes", "dit_ulysses_pack_uneven",
     "dit_ulysses_unpack_uneven", "dit_ring_anything_pad", "dit_ring_anything_trim",
@@ -136,6 +137,29 @@ def dit_ulysses_pack(layout: DitA2ALayout, direction: int, rank: int, planes, se
     arr = (ctypes.c_void_p * 3)(*[_dev(p, f"planes[{i}]") for i, p in enumerate(planes)])
     check(lib().dit_ulysses_pack(ctypes.byref(layout), direction, rank, arr, _dev(send, "send"),
                                  _stream(stream)), "dit_ulysses_pack")
+    return send
+
+
+def dit_ulysses_pack_convert(layout: DitA2ALayout, direction: int, rank: int, planes, send=None,
+                             stream=None):
+    """Pack float32 planes into a send buffer of the layout's 16-bit dtype
+    (bf16 or f16), rounding each element to nearest, ties to even; the maps
+    are those of dit_ulysses_pack."""
+    torch = _torch()
+    planes = list(planes)
+    if len(planes) != layout.n_planes:
+        raise ValueError(f"expected {layout.n_planes} planes, got {len(planes)}")
+    if layout.dtype not in (DIT_BF16, DIT_F16):
+        raise ValueError("the converting pack writes a bf16 or f16 send buffer")
+    dt, dev = _torch_dtype(layout.dtype), planes[0].device
+    _expect_all(planes, "planes", _plane_numel(layout, direction, True), torch.float32, dev)
+    if send is None:
+        send = torch.empty(_send_shape(layout), dtype=dt, device=dev)
+    _expect(send, "send", layout.U * layout.elems_per_peer, dt, dev)
+    arr = (ctypes.c_void_p * 3)(*[_dev(p, f"planes[{i}]") for i, p in enumerate(planes)])
+    check(lib().dit_ulysses_pack_convert(ctypes.byref(layout), direction, rank, arr,
+                                         _dev(send, "send"), _stream(stream)),
+          "dit_ulysses_pack_convert")
     return send
 
 

@@ -32,6 +32,7 @@ EXPORTS = (
     "dit_last_error",
     "dit_a2a_layout_init",
     "dit_ulysses_pack",
+    "dit_ulysses_pack_convert",
     "dit_ulysses_unpack",
     "dit_ulysses_unpack_rope",
     "dit_a2a_uneven_init",
@@ -122,6 +123,9 @@ def _declare(lib):
     lib.dit_ulysses_pack.restype = ctypes.c_int
     lib.dit_ulysses_pack.argtypes = [ctypes.POINTER(DitA2ALayout), ctypes.c_int, _I32,
                                      ctypes.POINTER(_P), _P, _P]
+    lib.dit_ulysses_pack_convert.restype = ctypes.c_int
+    lib.dit_ulysses_pack_convert.argtypes = [ctypes.POINTER(DitA2ALayout), ctypes.c_int, _I32,
+                                             ctypes.POINTER(_P), _P, _P]
     lib.dit_ulysses_unpack.restype = ctypes.c_int
     lib.dit_ulysses_unpack.argtypes = [ctypes.POINTER(DitA2ALayout), ctypes.c_int, _I32, _P,
                                        ctypes.POINTER(_P), _P]

@@ -214,6 +214,46 @@ dit_status_t dit_ulysses_unpack(const dit_a2a_layout* layout, dit_a2a_dir_t dir,
   return run_permute(layout, (int)dir, rank, false, nullptr, recv_buf, out_planes, nullptr, stream);
 }
 
+dit_status_t dit_ulysses_pack_convert(const dit_a2a_layout* L, dit_a2a_dir_t dir, int32_t rank,
+                                      const void* const* in_planes, void* send_buf, void* stream) {
+  dit_status_t st = check_permute(L, (int)dir, rank);
+  if (st != DIT_OK) return st;
+  if (L->dtype != DIT_BF16 && L->dtype != DIT_F16)
+    return fail(DIT_ERR_UNSUPPORTED, "the converting pack writes a bf16 or f16 send buffer "
+                                     "(layout dtype %d)", (int)L->dtype);
+  const int64_t buf_elems = L->elems_per_peer * L->U;
+  const int64_t plane_elems = dir == DIT_SEQ_TO_HEAD ? (int64_t)L->B * L->S_loc * L->H * L->D
+                                                     : (int64_t)L->B * L->S * L->H_loc * L->D;
+  if (buf_elems == 0 && plane_elems == 0) {
+    clear_error();
+    return DIT_OK;
+  }
+  if (in_planes == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "in_planes array is NULL");
+  if (send_buf == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "send_buf is NULL");
+  if (!aligned(send_buf, 2)) return fail(DIT_ERR_UNSUPPORTED, "send_buf not 2-byte aligned");
+  for (int i = 0; i < L->n_planes; ++i) {
+    if (in_planes[i] == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "in_planes[%d] is NULL", i);
+    if (!aligned(in_planes[i], 4))
+      return fail(DIT_ERR_UNSUPPORTED, "in_planes[%d] not 4-byte aligned", i);
+    if (overlap(in_planes[i], (size_t)plane_elems * 4, send_buf, (size_t)buf_elems * 2))
+      return fail(DIT_ERR_INVALID_ARGUMENT, "plane %d overlaps the send buffer", i);
+  }
+  dit::PermuteArgs a;
+  for (int i = 0; i < 3; ++i) {
+    a.in[i] = i < L->n_planes ? in_planes[i] : nullptr;
+    a.out[i] = nullptr;
+  }
+  a.out[0] = send_buf;
+  a.B = L->B; a.S = L->S; a.H = L->H; a.D = L->D; a.U = L->U; a.n_planes = L->n_planes;
+  a.S_loc = L->S_loc; a.H_loc = L->H_loc; a.rank = rank;
+  a.elem_bytes = 4;
+  const dit::PermuteKind kind = dir == DIT_SEQ_TO_HEAD ? dit::PACK_SEQ_TO_HEAD : dit::PACK_HEAD_TO_SEQ;
+  st = hip_status(dit::launch_pack_convert(kind, a, L->dtype == DIT_BF16, (hipStream_t)stream),
+                  "converting pack launch");
+  if (st == DIT_OK) clear_error();
+  return st;
+}
+
 dit_status_t dit_ulysses_unpack_rope(const dit_a2a_layout* L, int32_t rank, const void* recv_buf,
                                      void* const* out_planes, const float* rope_cos,
                                      const float* rope_sin, void* stream) {
@@ -617,6 +657,8 @@ dit_status_t dit_ulysses_unpack_fp8(const dit_a2a_layout* L, dit_a2a_dir_t dir, 
   return run_fp8(L, (int)dir, rank, false, (const void* const*)out_planes, recv_buf, stream);
 }
 
+}  // extern "C"
+
 namespace {
 
 // Checks shared by every attention call and the workspace size query.
@@ -752,6 +794,8 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
 }
 
 }  // namespace
+
+extern "C" {
 
 dit_status_t dit_attn_workspace_size(int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D,
                                      dit_dtype_t in_dtype, dit_dtype_t o_dtype, int32_t merge,

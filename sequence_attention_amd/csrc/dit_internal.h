@@ -56,6 +56,10 @@ struct PermuteArgs {
 };
 
 hipError_t launch_permute(PermuteKind kind, const PermuteArgs& a, hipStream_t stream);
+// The two pack kinds over float32 planes into a 16-bit send buffer (bf16 or
+// f16, round to nearest even); elem_bytes is ignored.
+hipError_t launch_pack_convert(PermuteKind kind, const PermuteArgs& a, bool to_bf16,
+                               hipStream_t stream);
 
 // Per-peer chunk copies between planes and a buffer of back-to-back chunks
 // of per-peer sizes (padding-free Ulysses maps, Ring Anything pad / trim).

@@ -185,6 +185,46 @@ hipError_t launch_kind(const PermuteGeom& g, int vec_bytes, hipStream_t stream) 
   return hipGetLastError();
 }
 
+// The packs with a conversion on the way in (edge-dit.cpp "Parallel
+// execution": the packed QKV operator's optional F32-to-F16 conversion, and
+// F16 / BF16 output produced directly on the head-to-sequence path).  The
+// planes are float32, the send buffer 16-bit: each thread reads E floats
+// through the same index maps as the plain packs (a "vector" is E elements
+// on both sides) and stores the E rounded values at out[0] + v.  The packed
+// hardware conversions round to nearest, ties to even, keep subnormals
+// (the kernel runs with f32 and f16 denormals preserved), send overflow to
+// infinity and NaN to a quiet NaN.
+template <int KIND, int E, bool kBf16>
+__global__ __launch_bounds__(kThreads) void pack_convert_kernel(PermuteGeom g) {
+  typedef float SV __attribute__((ext_vector_type(E)));
+  typedef __bf16 BV __attribute__((ext_vector_type(E)));
+  typedef _Float16 HV __attribute__((ext_vector_type(E)));
+  const uint32_t v = blockIdx.x * kThreads + threadIdx.x;
+  if (v >= g.total_vecs) return;
+  SV* unused;
+  SV x;
+  if constexpr (KIND == PACK_SEQ_TO_HEAD) x = pack_s2h<SV>(g, v, &unused);
+  else x = pack_h2s<SV>(g, v, &unused);
+  if constexpr (kBf16) {
+    store_nt(reinterpret_cast<BV*>(g.out[0]) + v, __builtin_convertvector(x, BV));
+  } else {
+    store_nt(reinterpret_cast<HV*>(g.out[0]) + v, __builtin_convertvector(x, HV));
+  }
+}
+
+template <int KIND, bool kBf16>
+hipError_t launch_convert_kind(const PermuteGeom& g, int E, hipStream_t stream) {
+  const uint32_t blocks = (g.total_vecs + kThreads - 1) / kThreads;
+  if (blocks == 0) return hipSuccess;
+  switch (E) {
+    case 8: pack_convert_kernel<KIND, 8, kBf16><<<blocks, kThreads, 0, stream>>>(g); break;
+    case 4: pack_convert_kernel<KIND, 4, kBf16><<<blocks, kThreads, 0, stream>>>(g); break;
+    case 2: pack_convert_kernel<KIND, 2, kBf16><<<blocks, kThreads, 0, stream>>>(g); break;
+    default: pack_convert_kernel<KIND, 1, kBf16><<<blocks, kThreads, 0, stream>>>(g); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_permute(PermuteKind kind, const PermuteArgs& a, hipStream_t stream) {
@@ -231,6 +271,38 @@ hipError_t launch_permute(PermuteKind kind, const PermuteArgs& a, hipStream_t st
     case PACK_HEAD_TO_SEQ: return launch_kind<PACK_HEAD_TO_SEQ>(g, vec, stream);
     default: return launch_kind<UNPACK_HEAD_TO_SEQ>(g, vec, stream);
   }
+}
+
+hipError_t launch_pack_convert(PermuteKind kind, const PermuteArgs& a, bool to_bf16,
+                               hipStream_t stream) {
+  // E elements per thread: the most that divides a head and keeps every
+  // float32 load (4E bytes) and 16-bit store (2E bytes) aligned.
+  uint32_t in_bits = 0, out_bits = (uint32_t)(uintptr_t)a.out[0];
+  for (int i = 0; i < a.n_planes; ++i) in_bits |= (uint32_t)(uintptr_t)a.in[i];
+  int E = 8;
+  while (E > 1 && (a.D % E != 0 || in_bits % (4 * E) != 0 || out_bits % (2 * E) != 0)) E >>= 1;
+
+  PermuteGeom g;
+  for (int i = 0; i < 3; ++i) {
+    g.in[i] = static_cast<const char*>(a.in[i]);
+    g.out[i] = static_cast<char*>(a.out[i]);
+  }
+  g.B = a.B; g.S = a.S; g.H = a.H; g.D = a.D; g.U = a.U; g.n_planes = a.n_planes;
+  g.S_loc = a.S_loc; g.H_loc = a.H_loc; g.rank = a.rank;
+  g.head_vecs = a.D / E;
+  g.run_vecs = g.head_vecs * a.H_loc;
+  if (g.run_vecs == 0) return hipSuccess;
+  g.div_run = make_fastdiv(g.run_vecs);
+  g.div_a = make_fastdiv(a.S_loc > 0 ? a.S_loc : 1);
+  g.div_b = make_fastdiv(a.B > 0 ? a.B : 1);
+  g.div_c = make_fastdiv(a.n_planes);
+  const uint64_t rows = (uint64_t)a.U * a.n_planes * a.B * a.S_loc;
+  g.total_vecs = (uint32_t)(rows * g.run_vecs);  // < 2^31: checked by the ABI layer
+  if (kind == PACK_SEQ_TO_HEAD)
+    return to_bf16 ? launch_convert_kind<PACK_SEQ_TO_HEAD, true>(g, E, stream)
+                   : launch_convert_kind<PACK_SEQ_TO_HEAD, false>(g, E, stream);
+  return to_bf16 ? launch_convert_kind<PACK_HEAD_TO_SEQ, true>(g, E, stream)
+                 : launch_convert_kind<PACK_HEAD_TO_SEQ, false>(g, E, stream);
 }
 
 }  // namespace dit

@@ -156,6 +156,34 @@ def test_unpack_rope_rejects(lib):
     assert f(ctypes.byref(empty), 0, NULL, _planes(0, 0, 0), NULL, NULL, NULL) == 0
 
 
+def test_pack_convert_rejects(lib):
+    # B=1, S=8, H=4, D=8, U=2, 3 planes: f32 planes of 1*4*4*8*4 = 512 B,
+    # a bf16 send buffer of 2*3*1*4*2*8*2 = 768 B
+    L = _layout(lib, 1, 8, 4, 8, 2, 1, 3, 0)
+    ok3 = _planes(A, A + 4096, A + 8192)
+    send = P(A + 65536)
+    f = lib.dit_ulysses_pack_convert
+    assert f(None, 0, 0, ok3, send, NULL) == INV
+    assert f(ctypes.byref(L), 2, 0, ok3, send, NULL) == INV              # direction
+    assert f(ctypes.byref(L), 0, 2, ok3, send, NULL) == INV              # rank == U
+    assert f(ctypes.byref(L), 0, 0, None, send, NULL) == INV             # plane array
+    assert f(ctypes.byref(L), 0, 0, _planes(A, 0, A + 8192), send, NULL) == INV
+    assert f(ctypes.byref(L), 0, 0, ok3, NULL, NULL) == INV              # send buffer
+    assert f(ctypes.byref(L), 0, 0, _planes(A + 2, A + 4096, A + 8192), send, NULL) == UNS
+    assert f(ctypes.byref(L), 0, 0, ok3, P(A + 65537), NULL) == UNS      # odd send address
+    assert f(ctypes.byref(L), 0, 0, ok3, P(A + 4096 + 256), NULL) == INV  # overlaps plane 1
+    assert "overlap" in lib.dit_last_error().decode()
+    f32 = _layout(lib, 1, 8, 4, 8, 2, 1, 3, 2)                            # 32-bit send buffer
+    assert f(ctypes.byref(f32), 0, 0, ok3, send, NULL) == UNS
+    bad = _lib.DitA2ALayout.from_buffer_copy(L)
+    bad.H_loc += 1
+    assert f(ctypes.byref(bad), 0, 0, ok3, send, NULL) == INV
+    huge = _layout(lib, 1, 2**21, 1024, 128, 2, 1, 3, 1)                  # >= 2^31 elements
+    assert f(ctypes.byref(huge), 0, 0, ok3, send, NULL) == UNS
+    empty = _layout(lib, 0, 8, 4, 8, 2, 1, 3, 1)
+    assert f(ctypes.byref(empty), 1, 1, _planes(0, 0, 0), NULL, NULL) == 0
+
+
 def test_empty_exchange_is_a_no_op(lib):
     L = _layout(lib, 0, 8, 4, 8, 2, 1, 3, 0)
     assert lib.dit_ulysses_pack(ctypes.byref(L), 0, 0, _planes(0, 0, 0), NULL, NULL) == 0

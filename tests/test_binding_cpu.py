@@ -45,6 +45,21 @@ def test_pack_rejects_planes_on_two_devices():
         sa.dit_ulysses_pack(L3, sa.DIT_SEQ_TO_HEAD, 0, planes)
 
 
+def test_pack_convert_checks_plane_dtype_and_send_buffer():
+    planes = [_t(1, 5, 4, 64, dtype=torch.float32) for _ in range(3)]
+    with pytest.raises(ValueError, match=r"planes\[0\]: dtype"):
+        sa.dit_ulysses_pack_convert(L3, sa.DIT_SEQ_TO_HEAD, 0, [_t(1, 5, 4, 64)] * 3)
+    with pytest.raises(ValueError, match=r"planes\[2\]: .* elements"):
+        sa.dit_ulysses_pack_convert(L3, sa.DIT_SEQ_TO_HEAD, 0,
+                                    planes[:2] + [_t(1, 5, 4, 63, dtype=torch.float32)])
+    with pytest.raises(ValueError, match="send: dtype"):
+        sa.dit_ulysses_pack_convert(L3, sa.DIT_SEQ_TO_HEAD, 0, planes,
+                                    send=_t(2, 3, 1, 5, 2, 64, dtype=torch.float16))
+    with pytest.raises(ValueError, match="bf16 or f16"):
+        sa.dit_ulysses_pack_convert(sa.dit_a2a_layout_init(1, 10, 4, 64, 2, 1, 3, torch.float32),
+                                    sa.DIT_SEQ_TO_HEAD, 0, planes)
+
+
 def test_unpack_checks_receive_buffer_and_outputs():
     with pytest.raises(ValueError, match="recv: .* elements"):
         sa.dit_ulysses_unpack(L3, sa.DIT_SEQ_TO_HEAD, 0, _t(2, 3, 1, 5, 2, 32))
