@@ -2,7 +2,7 @@
  * dit_attn.h -- C ABI of the per-GPU hot path of sequence-parallel DiT
  * attention on AMD Instinct MI355X (gfx950).
  *
- * One rank's share of a Ulysses x ring split is computed by five kinds of
+ * One rank's share of a Ulysses x ring split is computed by these kinds of
  * call:
  *   dit_ulysses_pack / dit_ulysses_unpack  layout transforms around the
  *                                          Ulysses all-to-alls
@@ -17,6 +17,8 @@
  *                                          sequence shards
  *   dit_ulysses_pack_fp8 / _unpack_fp8     the Ulysses maps with Q, V and O
  *                                          exchanged as FP8 (K kept bf16)
+ *   dit_attn_fwd_send                      attention that stores O straight into
+ *                                          the head-to-sequence send buffer
  *   dit_attn_fwd, dit_attn_fwd_ws          attention with per-row LSE (_ws:
  *                                          with a caller workspace that lets
  *                                          the kernel split the last round)
@@ -443,6 +445,37 @@ dit_status_t dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* 
                              int32_t B, int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale,
                              dit_dtype_t in_dtype, dit_dtype_t o_dtype, void* workspace,
                              int64_t workspace_bytes, void* stream);
+
+/*
+ * Attention of Ulysses rank `rank` with O stored straight into the
+ * head-to-sequence send buffer (edge-dit.cpp "Parallel execution": the
+ * packed head-to-sequence operator partitions the attention output by
+ * destination sequence shard into a peer-major send buffer; here attention
+ * writes that buffer itself, so the separate pack and its read and write of
+ * O disappear).  The result equals, bit for bit,
+ *   dit_attn_fwd_ws(q, k, v, o, lse, B, S, Skv, H_loc, D, scale, BF16, BF16,
+ *                   workspace, workspace_bytes)
+ *   followed by dit_ulysses_pack(layout, DIT_HEAD_TO_SEQ, rank, {o}, send_buf):
+ *   send[p,0,b,s,h',d] = O[b, p*S_loc + s, h', d] for p*S_loc + s < S and
+ *   rank*H_loc + h' < H, else 0 (pad rows and pad heads are written as 0).
+ *
+ * layout: from dit_a2a_layout_init with n_planes = 1 and dtype DIT_BF16;
+ *   B, S, H_loc and D of the call come from it.
+ * q: [B, S, H_loc, D] bf16 (the head-sharded queries of this rank);
+ * k, v: [B, Skv, H_loc, D] bf16; lse: [B, H_loc, S] fp32 or NULL;
+ * send_buf: [U, 1, B, S_loc, H_loc, D] bf16, every element written.
+ * workspace, workspace_bytes: as dit_attn_fwd_ws (sized by
+ *   dit_attn_workspace_size(B, S, Skv, H_loc, D, BF16, BF16, 0, ...)).
+ * Skv = 0 writes a zero buffer and LSE = -inf.  Uses no memory beyond its
+ * arguments.
+ * Errors: INVALID_ARGUMENT (as dit_ulysses_pack for the layout and rank,
+ *   n_planes != 1, and as dit_attn_fwd_ws for the tensors, with the whole
+ *   send buffer as the output); UNSUPPORTED (layout dtype not bf16, and as
+ *   dit_attn_fwd); HIP.
+ */
+dit_status_t dit_attn_fwd_send(const void* q, const void* k, const void* v, void* send_buf,
+                               float* lse, const dit_a2a_layout* layout, int32_t rank, int32_t Skv,
+                               float scale, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

@@ -34,7 +34,7 @@ __all__ = [
     "dit_ulysses_unpack_uneven", "dit_ring_anything_pad", "dit_ring_anything_trim",
     "DitA2AUnevenLayout",
     "dit_a2a_fp8_bytes_per_peer", "dit_ulysses_pack_fp8", "dit_ulysses_unpack_fp8",
-    "dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_noalloc", "dit_attn_workspace_size", "dit_attn_fwd_kvlen", "dit_attn_merge",
+    "dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_send", "dit_attn_fwd_noalloc", "dit_attn_workspace_size", "dit_attn_fwd_kvlen", "dit_attn_merge",
     "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
@@ -480,6 +480,49 @@ def dit_attn_fwd_ws(q, k, v, workspace, o=None, lse=None, scale=None, o_dtype=No
         raise ValueError("workspace must be a uint8 tensor")
     return dit_attn_fwd(q, k, v, o=o, lse=lse, scale=scale, o_dtype=o_dtype, stream=stream,
                         workspace=workspace)
+
+
+def dit_attn_fwd_send(q, k, v, layout: DitA2ALayout, rank: int, send=None, lse=None, scale=None,
+                      want_lse=True, stream=None, workspace=True):
+    """Attention of Ulysses rank `rank` with O stored straight into the
+    head-to-sequence send buffer [U, 1, B, S_loc, H_loc, D] (bf16): equal,
+    bit for bit, to dit_attn_fwd_ws followed by dit_ulysses_pack(layout,
+    DIT_HEAD_TO_SEQ, rank, [O]).  q is [B, S, H_loc, D], k / v are
+    [B, Skv, H_loc, D] (bf16); layout has n_planes = 1 and dtype bf16.
+    Returns (send, LSE [B, H_loc, S] or None)."""
+    torch = _torch()
+    B, Sq, Skv, H, D = _check_qkv(q, k, v)
+    if layout.n_planes != 1 or layout.dtype != DIT_BF16:
+        raise ValueError("the send layout must have n_planes = 1 and dtype bf16")
+    if (B, Sq, H, D) != (layout.B, layout.S, layout.H_loc, layout.D):
+        raise ValueError(f"q {tuple(q.shape)} does not match the layout "
+                         f"[B={layout.B}, S={layout.S}, H_loc={layout.H_loc}, D={layout.D}]")
+    if q.dtype != torch.bfloat16:
+        raise ValueError(f"q: dtype {q.dtype}, expected bfloat16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if send is None:
+        send = torch.empty(_send_shape(layout), dtype=torch.bfloat16, device=q.device)
+    _expect(send, "send", layout.U * layout.elems_per_peer, torch.bfloat16, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, "lse", B * H * Sq, torch.float32, q.device)
+    st = _stream(stream)
+    if workspace is True:
+        workspace = _workspace(dit_attn_workspace_size(B, Sq, Skv, H, D, DIT_BF16, DIT_BF16),
+                               q.device, st)
+    elif workspace is False:
+        workspace = None
+    elif workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    ws_ptr, ws_bytes = (ctypes.c_void_p(0), 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                                         workspace.numel())
+    lse_ptr = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
+    check(lib().dit_attn_fwd_send(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(send, "send"), lse_ptr,
+                                  ctypes.byref(layout), rank, Skv, float(scale), ws_ptr, ws_bytes, st),
+          "dit_attn_fwd_send")
+    return send, lse
 
 
 def dit_attn_fwd_noalloc(q, k, v, o, lse, scale=None, stream=None):

@@ -91,7 +91,23 @@ struct Params {
   uint32_t split;    // pieces per tile of the split round (>= 2 when used)
   uint32_t split_wgs;  // workgroups of the split round: split x (tiles - n_whole)
   float scale;
+  // Where O goes: send_rows == 0: [B, Sq, H, D].  Otherwise the peer-major
+  // head-to-sequence send buffer [U, 1, B, send_rows, H, D]: query row t is
+  // row t % send_rows of peer t / send_rows's chunk, and heads at or past
+  // o_heads (pad heads) are stored as zeros.
+  int32_t send_rows;
+  int32_t send_batches;
+  int32_t o_heads;
 };
+
+// Element offset of the first dim of query row q_row of batch b in O
+// (row stride rs = H * D elements).
+__device__ __forceinline__ size_t o_row_offset(const Params& p, int b, int q_row, size_t rs) {
+  if (p.send_rows == 0) return ((size_t)b * p.Sq + q_row) * rs;
+  const int peer = q_row / p.send_rows;
+  const int s = q_row - peer * p.send_rows;
+  return (((size_t)peer * p.send_batches + b) * p.send_rows + s) * rs;
+}
 
 // Workgroups are dealt round-robin over the XCDs; renumber them so that each
 // XCD owns one contiguous range of logical indices (a bijection on [0, n)).
@@ -392,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       // accumulator left as it is
       if constexpr (!kMerge) {
         if (q_row < p.Sq) {
-          const size_t orow = ((size_t)b * p.Sq + q_row) * rs + (size_t)h * D;
+          const size_t orow = o_row_offset(p, b, q_row, rs) + (size_t)h * D;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -433,7 +449,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       const float ltot = l_lane + __shfl_xor(l_lane, 32);
       const float lrtot = lr_lane + __shfl_xor(lr_lane, 32);
       if (!q_ok) return;
-      const size_t orow = ((size_t)b * p.Sq + q_row) * rs + (size_t)h * D;
+      const size_t orow = o_row_offset(p, b, q_row, rs) + (size_t)h * D;
+      const bool pad_head = h >= p.o_heads;
       const size_t lse_idx = ((size_t)b * p.H + h) * p.Sq + q_row;
       const float l_c = m_ref * p.scale + __logf(ltot);
       float cc = 1.0f / lrtot, ca = 0.0f, l_new = l_c;
@@ -470,6 +487,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(ca, prev[e], o[e]);
             }
+          }
+          if (pad_head) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = 0.0f;
           }
           if constexpr (kOutF32) {
             *reinterpret_cast<float4*>(static_cast<float*>(p.o) + orow + d) = make_float4(o[0], o[1], o[2], o[3]);
@@ -631,6 +652,9 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.n_qtiles = (a.Sq + kBM - 1) / kBM;
   p.nblocks = (a.Skv + kBN - 1) / kBN;
   p.scale = a.scale;
+  p.send_rows = a.send_rows;
+  p.send_batches = a.B;
+  p.o_heads = a.send_rows > 0 ? a.o_heads : a.H;
   if (pl.n_tiles == 0 || p.nblocks == 0) return hipSuccess;
   // without (enough) workspace every tile is taken whole
   const bool split = pl.split > 1 && a.workspace != nullptr && a.workspace_bytes >= pl.ws_bytes;

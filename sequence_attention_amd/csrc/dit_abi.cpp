@@ -4,6 +4,7 @@
 // error path on a machine without a GPU).  The library keeps no state apart
 // from the calling thread's last error text and per-device facts (compute
 // unit count, kernel occupancy) cached on first use.
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -714,7 +715,8 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
                        int32_t Sq, int32_t Skv, int32_t H, int32_t D, float scale, dit_dtype_t in_dtype,
                        dit_dtype_t o_dtype, void* stream, bool merge, const int32_t* kv_len = nullptr,
                        bool has_kv_len = false, void* workspace = nullptr, int64_t workspace_bytes = 0,
-                       bool static_scratch = false) {
+                       bool static_scratch = false, const dit_a2a_layout* send = nullptr,
+                       int32_t send_rank = 0) {
   dit_status_t st = check_attn_shape(B, Sq, Skv, H, D, in_dtype, o_dtype);
   if (st != DIT_OK) return st;
   if (!(scale > 0.0f) || !isfinite(scale))
@@ -740,7 +742,9 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
   const int eb = dtype_bytes(in_dtype);
   const size_t q_bytes = (size_t)B * Sq * H * D * eb;
   const size_t kv_bytes = (size_t)B * Skv * H * D * eb;
-  const size_t o_bytes = (size_t)B * Sq * H * D * dtype_bytes(o_dtype);
+  // O is [B, Sq, H, D], or the whole send buffer [U, 1, B, S_loc, H, D]
+  const size_t o_bytes = send != nullptr ? (size_t)send->U * send->elems_per_peer * 2
+                                         : (size_t)B * Sq * H * D * dtype_bytes(o_dtype);
   if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, k, kv_bytes) ||
       overlap(o, o_bytes, v, kv_bytes) ||
       (lse != nullptr && overlap(lse, (size_t)B * H * Sq * 4, o, o_bytes)))
@@ -757,9 +761,21 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
     clear_error();
     return DIT_OK;
   }
+  if (send != nullptr && Skv == 0) {  // O = 0 everywhere, pads included; LSE = -inf
+    hipError_t e = dit::launch_fill_words(o, o_bytes / 4, 0u, (hipStream_t)stream);
+    if (e == hipSuccess && lse != nullptr)
+      e = dit::launch_fill_words(lse, (uint64_t)B * H * Sq, 0xFF800000u, (hipStream_t)stream);
+    st = hip_status(e, "empty attention fill");
+    if (st == DIT_OK) clear_error();
+    return st;
+  }
   dit::AttnArgs a = attn_args(B, Sq, Skv, H, D, scale, o_dtype, merge);
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.kv_len = has_kv_len ? kv_len : nullptr;
+  if (send != nullptr) {
+    a.send_rows = send->S_loc;
+    a.o_heads = std::max(0, std::min(send->H_loc, send->H - send_rank * send->H_loc));
+  }
   if (workspace != nullptr) {
     size_t need = 0;
     if ((st = attn_workspace_need(a, in_dtype, has_kv_len, &need)) != DIT_OK) return st;
@@ -788,6 +804,10 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
   if (Skv == 0) e = dit::launch_attn_empty(a, in_dtype == DIT_F32, (hipStream_t)stream);
   else if (in_dtype == DIT_BF16) e = dit::launch_attn_fwd_bf16(a, (hipStream_t)stream);
   else e = dit::launch_attn_fwd_f32(a, (hipStream_t)stream);
+  // pad rows of the padded sequence have no query: zero them in the buffer
+  if (e == hipSuccess && send != nullptr && (int64_t)send->U * send->S_loc > Sq)
+    e = dit::launch_send_rows_zero(o, B, send->S_loc, Sq, send->U * send->S_loc, (int64_t)H * D,
+                                   (hipStream_t)stream);
   st = hip_status(e, "attention launch");
   if (st == DIT_OK) clear_error();
   return st;
@@ -818,6 +838,21 @@ dit_status_t dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* 
                              int64_t workspace_bytes, void* stream) {
   return attn_call(q, k, v, o, lse, B, Sq, Skv, H, D, scale, in_dtype, o_dtype, stream, false, nullptr,
                    false, workspace, workspace_bytes);
+}
+
+dit_status_t dit_attn_fwd_send(const void* q, const void* k, const void* v, void* send_buf, float* lse,
+                               const dit_a2a_layout* layout, int32_t rank, int32_t Skv, float scale,
+                               void* workspace, int64_t workspace_bytes, void* stream) {
+  dit_status_t st = check_permute(layout, DIT_HEAD_TO_SEQ, rank);
+  if (st != DIT_OK) return st;
+  if (layout->n_planes != 1)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "the send buffer holds one plane (O); layout has n_planes = %d",
+                layout->n_planes);
+  if (layout->dtype != DIT_BF16)
+    return fail(DIT_ERR_UNSUPPORTED, "attention into the send buffer is served for bf16 only");
+  return attn_call(q, k, v, send_buf, lse, layout->B, layout->S, Skv, layout->H_loc, layout->D, scale,
+                   DIT_BF16, DIT_BF16, stream, false, nullptr, false, workspace, workspace_bytes, false,
+                   layout, rank);
 }
 
 dit_status_t dit_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,

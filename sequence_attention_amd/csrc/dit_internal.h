@@ -141,7 +141,20 @@ struct AttnArgs {
   // slots), or null: tiles are then never split.
   void* workspace = nullptr;
   size_t workspace_bytes = 0;
+  // bf16 path only: send_rows > 0 stores O in the head-to-sequence send
+  // buffer [U, 1, B, send_rows, H, D] (query row t -> peer t / send_rows,
+  // row t % send_rows), heads at or past o_heads as zeros.
+  int32_t send_rows = 0;
+  int32_t o_heads = 0;
 };
+
+// Zero rows [t0, t1) (t1 <= U * S_loc) of every batch of a bf16 send buffer
+// [U, 1, B, S_loc, row_elems] (row t -> peer t / S_loc, row t % S_loc);
+// row_elems * 2 bytes must be a multiple of 16.
+hipError_t launch_send_rows_zero(void* send, int32_t B, int32_t S_loc, int32_t t0, int32_t t1,
+                                 int64_t row_elems, hipStream_t stream);
+// Write `value` into n 32-bit words.
+hipError_t launch_fill_words(void* p, uint64_t n, uint32_t value, hipStream_t stream);
 
 // Bytes of workspace the bf16 path uses for this call on the current device
 // (0: no tile is split).  Host-only queries of the device.

@@ -273,6 +273,40 @@ def test_attn_ws_empty_is_a_no_op(lib):
     assert _attn_ws(lib, ws=0, ws_bytes=0, q=0, k=0, v=0, o=0, lse=0, B=0) == 0
 
 
+def test_attn_fwd_send_rejects(lib):
+    # B=1, S=64, H=4, D=64 bf16, U=2: q [1,64,2,64] = 16 KiB, send 16 KiB
+    L = _layout(lib, 1, 64, 4, 64, 2, 1, 1, 0)
+    f = lib.dit_attn_fwd_send
+    q, k, v, send, lse = P(A), P(A + 2**20), P(A + 2**21), P(A + 2**22), P(A + 2**23)
+
+    def call(layout=ctypes.byref(L), rank=0, Skv=64, scale=0.125, send_=send, q_=q, ws=NULL, wsb=0):
+        return f(q_, k, v, send_, ctypes.cast(lse, ctypes.POINTER(ctypes.c_float)), layout, rank, Skv,
+                 scale, ws, wsb, NULL)
+
+    assert call(layout=None) == INV
+    assert call(rank=2) == INV
+    assert call(rank=-1) == INV
+    assert call(Skv=-1) == INV
+    assert call(scale=0.0) == INV
+    assert call(q_=NULL) == INV
+    assert call(send_=NULL) == INV
+    assert call(send_=P(A + 8192)) == INV                                  # send overlaps q
+    assert call(send_=P(A + 2**22 + 8)) == UNS                             # misaligned
+    assert call(ws=P(A + 2**24 + 64), wsb=4096) == UNS                     # workspace alignment
+    assert call(ws=NULL, wsb=64) == INV
+    L3 = _layout(lib, 1, 64, 4, 64, 2, 1, 3, 0)
+    assert call(layout=ctypes.byref(L3)) == INV                            # n_planes must be 1
+    Lh = _layout(lib, 1, 64, 4, 64, 2, 1, 1, 1)
+    assert call(layout=ctypes.byref(Lh)) == UNS                            # f16 buffer
+    Ld = _layout(lib, 1, 64, 4, 96, 2, 1, 1, 0)
+    assert call(layout=ctypes.byref(Ld)) == UNS                            # head dim
+    bad = _lib.DitA2ALayout.from_buffer_copy(L)
+    bad.S_loc += 1
+    assert call(layout=ctypes.byref(bad)) == INV
+    empty = _layout(lib, 0, 64, 4, 64, 2, 1, 1, 0)
+    assert call(layout=ctypes.byref(empty), q_=NULL, send_=NULL) == 0
+
+
 def _ws_size(lib, B=1, Sq=128, Skv=128, H=2, D=64, din=0, dout=0, merge=0, out=True):
     n = ctypes.c_int64(-5)
     st = lib.dit_attn_workspace_size(B, Sq, Skv, H, D, din, dout, merge, ctypes.byref(n) if out else None)
