@@ -582,6 +582,22 @@ dit_status_t dit_attn_fwd_merge(const void* q, const void* k, const void* v, voi
 dit_status_t dit_cfg_combine(const void* p_uncond, const void* p_cond, void* out, int64_t n,
                              float g, dit_dtype_t dtype, void* stream);
 
+/*
+ * Measurement aid (not a step of the method): reports the shader clock.
+ * Launches `workgroups` workgroups of 256 threads; each runs `spin`
+ * iterations of a loop and writes, at out[2*i] and out[2*i+1], the shader
+ * cycles (s_memtime) and the ticks of the 100 MHz real-time counter
+ * (s_memrealtime) that elapsed in workgroup i.  The clock in GHz is
+ * cycles / ticks / 10.  mfma = 0: the loop is two dependent FMAs (a light
+ * load); mfma = 1: four independent bf16 32x32x16 MFMAs per wave (the
+ * matrix-core load of attention, under which the power limit sets the
+ * clock).  out: device memory of 2 * workgroups int64, 8-byte aligned.
+ * Errors: INVALID_ARGUMENT (workgroups outside [1, 65536], spin < 0, mfma
+ * not 0 or 1, out NULL); UNSUPPORTED (alignment); HIP.
+ */
+dit_status_t dit_clock_probe(int64_t* out, int32_t workgroups, int32_t spin, int32_t mfma,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ __all__ = [
     "DitA2AUnevenLayout",
     "dit_a2a_fp8_bytes_per_peer", "dit_ulysses_pack_fp8", "dit_ulysses_unpack_fp8",
     "dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_send", "dit_attn_fwd_noalloc", "dit_attn_workspace_size", "dit_attn_fwd_kvlen", "dit_attn_merge",
-    "dit_attn_fwd_merge", "dit_cfg_combine", "DitA2ALayout", "DitError",
+    "dit_attn_fwd_merge", "dit_cfg_combine", "dit_clock_probe", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
 
@@ -624,3 +624,16 @@ def dit_cfg_combine(p_uncond, p_cond, g: float, out=None, stream=None):
                                 p_uncond.numel(), float(g), _dtype_code(p_uncond.dtype),
                                 _stream(stream)), "dit_cfg_combine")
     return out
+
+
+def dit_clock_probe(workgroups=256, spin=20000, mfma=False, stream=None):
+    """Shader clock in GHz seen by `workgroups` probe workgroups (median,
+    min, max) under a light FMA load or (mfma=True) a bf16 MFMA load;
+    synchronizes the stream to read the result."""
+    torch = _torch()
+    out = torch.empty(2 * workgroups, dtype=torch.int64, device="cuda")
+    check(lib().dit_clock_probe(_dev(out, "out"), workgroups, spin, int(bool(mfma)), _stream(stream)),
+          "dit_clock_probe")
+    s = out.view(-1, 2).double().cpu()
+    ghz = (s[:, 0] / s[:, 1] / 10.0).sort().values
+    return {"median": float(ghz[len(ghz) // 2]), "min": float(ghz[0]), "max": float(ghz[-1])}

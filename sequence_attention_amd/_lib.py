@@ -53,6 +53,7 @@ EXPORTS = (
     "dit_attn_merge",
     "dit_attn_fwd_merge",
     "dit_cfg_combine",
+    "dit_clock_probe",
 )
 
 
@@ -178,6 +179,8 @@ def _declare(lib):
     lib.dit_attn_fwd_merge.restype = ctypes.c_int
     lib.dit_attn_fwd_merge.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                            ctypes.c_int, _P, ctypes.c_int64, _P]
+    lib.dit_clock_probe.restype = ctypes.c_int
+    lib.dit_clock_probe.argtypes = [_P, _I32, _I32, _I32, _P]
     lib.dit_cfg_combine.restype = ctypes.c_int
     lib.dit_cfg_combine.argtypes = [_P, _P, _P, ctypes.c_int64, ctypes.c_float, ctypes.c_int, _P]
 

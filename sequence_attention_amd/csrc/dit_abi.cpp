@@ -953,4 +953,17 @@ dit_status_t dit_cfg_combine(const void* p_uncond, const void* p_cond, void* out
   return st;
 }
 
+dit_status_t dit_clock_probe(int64_t* out, int32_t workgroups, int32_t spin, int32_t mfma, void* stream) {
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "workgroups=%d outside [1, 65536]", workgroups);
+  if (spin < 0) return fail(DIT_ERR_INVALID_ARGUMENT, "spin=%d < 0", spin);
+  if (mfma != 0 && mfma != 1) return fail(DIT_ERR_INVALID_ARGUMENT, "mfma=%d must be 0 or 1", mfma);
+  if (out == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (!aligned(out, 8)) return fail(DIT_ERR_UNSUPPORTED, "out not 8-byte aligned");
+  const dit_status_t st = hip_status(dit::launch_clock_probe(out, workgroups, spin, mfma != 0, (hipStream_t)stream),
+                                     "clock probe launch");
+  if (st == DIT_OK) clear_error();
+  return st;
+}
+
 }  // extern "C"

@@ -174,4 +174,9 @@ hipError_t launch_attn_fwd_f32(const AttnArgs& a, hipStream_t stream);
 // Skv == 0: O = 0, LSE = -inf.
 hipError_t launch_attn_empty(const AttnArgs& a, bool in_f32, hipStream_t stream);
 
+// ---- measurement aid ------------------------------------------------------------
+// out: [workgroups][2] int64 (shader cycles, 100 MHz real-time ticks).
+hipError_t launch_clock_probe(int64_t* out, int32_t workgroups, int32_t spin, bool mfma,
+                              hipStream_t stream);
+
 }  // namespace dit

@@ -534,3 +534,14 @@ def test_fp8_rejects(lib):
     assert pk(ctypes.byref(d16), 0, 0, ok3, buf, NULL) == UNS         # D not a multiple of 32
     empty = _layout(lib, 0, 8, 4, 32, 2, 1, 3, 0)
     assert pk(ctypes.byref(empty), 0, 0, _planes(0, 0, 0), NULL, NULL) == 0
+
+
+def test_clock_probe_rejects(lib):
+    f = lib.dit_clock_probe
+    out = ctypes.cast(P(A), ctypes.POINTER(ctypes.c_int64))
+    assert f(out, 0, 10, 0, NULL) == INV                     # no workgroups
+    assert f(out, 65537, 10, 0, NULL) == INV
+    assert f(out, 4, -1, 0, NULL) == INV                     # spin
+    assert f(out, 4, 10, 2, NULL) == INV                     # mode
+    assert f(None, 4, 10, 0, NULL) == INV
+    assert f(ctypes.cast(P(A + 4), ctypes.POINTER(ctypes.c_int64)), 4, 10, 1, NULL) == UNS
