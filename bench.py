@@ -84,6 +84,9 @@ def parse():
                     help="seconds of untimed steps before the warm-up steps, to bring the GPU clock up")
     ap.add_argument("--graph-launches", type=int, default=20,
                     help="launches captured per graph for the kernel timings")
+    ap.add_argument("--only", metavar="NAMES",
+                    help="comma-separated entries of `configs` to run alone (no step, no other part); "
+                         "for profiling one shape per run")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print the per-kernel table of a rocprofv3 kernel-trace database and exit")
     ap.add_argument("--pmc-summary", metavar="CSV",
@@ -250,6 +253,45 @@ class Step:
             launches[name]()
 
 
+def kernel_pools(w, torch, sa, step, rank):
+    """For each launch of the step, a function of the launch index over its
+    own rotated buffer sets (at least twice the Infinity Cache of that
+    launch's own traffic), so every kernel figure reads cold data."""
+    dev, bf16 = "cuda", torch.bfloat16
+    L3, L1 = step.L3, step.L1
+    S2H, H2S = sa.DIT_SEQ_TO_HEAD, sa.DIT_HEAD_TO_SEQ
+    kb = kernel_bytes(step)
+    o_b = w.B * w.S * L3.H_loc * w.D * 2
+    kb["BD_attention_send"] = 3 * o_b + kb["D_pack_o"] - o_b
+    kb["B_attention"] = 4 * o_b
+    shard = lambda: [torch.empty((w.B, L3.S_loc, w.H_total, w.D), dtype=bf16, device=dev).normal_()
+                     for _ in range(3)]
+    send3 = lambda: torch.empty((w.U, 3, w.B, L3.S_loc, L3.H_loc, w.D), dtype=bf16, device=dev).normal_()
+    heads = lambda n: [torch.empty((w.B, w.S, L3.H_loc, w.D), dtype=bf16, device=dev).normal_() for _ in range(n)]
+    send1 = lambda: torch.empty((w.U, 1, w.B, L1.S_loc, L1.H_loc, w.D), dtype=bf16, device=dev).normal_()
+    lse = lambda: torch.empty((w.B, L3.H_loc, w.S), dtype=torch.float32, device=dev)
+    out = lambda: torch.empty((w.B, L1.S_loc, w.H_total, w.D), dtype=bf16, device=dev)
+    cfg = lambda: torch.randn((3,) + CFG_SHAPE[1:], device=dev)
+    make = {
+        "A1_pack_qkv": (lambda: (shard(), send3()),
+                        lambda b: sa.dit_ulysses_pack(L3, S2H, rank, b[0], send=b[1])),
+        "A3_unpack_qkv": (lambda: (send3(), heads(3)),
+                          lambda b: sa.dit_ulysses_unpack(L3, S2H, rank, b[0], out=b[1])),
+        "BD_attention_send": (lambda: (heads(3), send1(), lse()),
+                              lambda b: sa.dit_attn_fwd_send(*b[0], L1, rank, send=b[1], lse=b[2], scale=w.scale,
+                                                             workspace=step.ws)),
+        "E_unpack_o": (lambda: (send1(), out()),
+                       lambda b: sa.dit_ulysses_unpack(L1, H2S, rank, b[0], out=[b[1]])),
+        "F_cfg": (cfg, lambda b: sa.dit_cfg_combine(b[0], b[1], 4.0, out=b[2])),
+        "B_attention": (lambda: (heads(4), lse()),
+                        lambda b: sa.dit_attn_fwd(*b[0][:3], o=b[0][3], lse=b[1], scale=w.scale,
+                                                  workspace=step.ws)),
+        "D_pack_o": (lambda: (heads(1), send1()),
+                     lambda b: sa.dit_ulysses_pack(L1, H2S, rank, b[0], send=b[1])),
+    }
+    return make, kb
+
+
 def kernel_bytes(step):
     """Algorithmic HBM bytes per launch: every input element read once and
     every output element written once (pad elements written count)."""
@@ -270,8 +312,11 @@ def kernel_bytes(step):
 # attention at every shard shape, and the ring
 # ---------------------------------------------------------------------------
 
-def attention_configs(torch, sa, workloads, launches, reps=20):
+def attention_configs(torch, sa, workloads, launches, reps=20, only=None):
     res = {}
+
+    def want(name):
+        return only is None or name in only
 
     def dev_randn(shape, seed):
         g = torch.Generator(device="cuda").manual_seed(seed)
@@ -282,6 +327,8 @@ def attention_configs(torch, sa, workloads, launches, reps=20):
         return torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
 
     for name in ("flux", "qwen_u4", "qwen_u5", "wan"):
+        if not want(f"attn_{name}"):
+            continue
         w = workloads.WORKLOADS[name]
         q = dev_randn((w.B, w.Sq, w.H, w.D), 1)
         k = dev_randn((w.B, w.Skv, w.H, w.D), 2)
@@ -301,6 +348,15 @@ def attention_configs(torch, sa, workloads, launches, reps=20):
         del q, k, v, o, lse, ws
 
     # ring shard: 4 K/V chunks of 4096 keys merged into one accumulator
+    ring_names = ("attn_ring_chunked_e2e", "attn_ring_fused_e2e", "attn_joint_text_image_ring_e2e",
+                  "attn_ring_chunk", "attn_ring_fused_hop", "attn_ring_unchunked")
+    if any(want(n) for n in ring_names):
+        ring_configs(torch, sa, workloads, launches, reps, want, dev_randn, ws_for, res)
+    qwen_permutes(torch, sa, workloads, launches, want, res)
+    return res
+
+
+def ring_configs(torch, sa, workloads, launches, reps, want, dev_randn, ws_for, res):
     rw = workloads.WORKLOADS["ring"]
     q = dev_randn((rw.B, rw.Sq, rw.H, rw.D), 4)
     k = dev_randn((rw.B, rw.Skv, rw.H, rw.D), 5)
@@ -334,16 +390,19 @@ def attention_configs(torch, sa, workloads, launches, reps=20):
 
     fl = rw.attn_flop()
     passes = max(2, launches // 4)
-    us = time_graph(torch, ring, passes, replays=2)
-    res["attn_ring_chunked_e2e"] = attn_roofline(
-        "ring_chunked_e2e", fl, us, chunks=rw.R, merges=rw.R - 1,
-        note="4 x attention [1,4096,24,128] x 4096 keys + 3 bf16 merges, hop order 0,3,2,1; "
-             "avg_launch_us is one whole pass")
-    us_f = time_graph(torch, ring_fused, passes, replays=2)
-    res["attn_ring_fused_e2e"] = attn_roofline(
-        "ring_fused_e2e", fl, us_f, chunks=rw.R,
-        note="hop 0 with dit_attn_fwd, hops 1-3 with dit_attn_fwd_merge (merge in the epilogue); "
-             "avg_launch_us is one whole pass")
+    us = us_f = None
+    if want("attn_ring_chunked_e2e"):
+        us = time_graph(torch, ring, passes, replays=2)
+        res["attn_ring_chunked_e2e"] = attn_roofline(
+            "ring_chunked_e2e", fl, us, chunks=rw.R, merges=rw.R - 1,
+            note="4 x attention [1,4096,24,128] x 4096 keys + 3 bf16 merges, hop order 0,3,2,1; "
+                 "avg_launch_us is one whole pass")
+    if want("attn_ring_fused_e2e"):
+        us_f = time_graph(torch, ring_fused, passes, replays=2)
+        res["attn_ring_fused_e2e"] = attn_roofline(
+            "ring_fused_e2e", fl, us_f, chunks=rw.R,
+            note="hop 0 with dit_attn_fwd, hops 1-3 with dit_attn_fwd_merge (merge in the epilogue); "
+                 "avg_launch_us is one whole pass")
     # joint text+image ring: the fused ring, then 300 valid of 512 replicated
     # text keys attended once and merged into the same accumulator
     k_txt = dev_randn((rw.B, 512, rw.H, rw.D), 7)
@@ -354,35 +413,45 @@ def attention_configs(torch, sa, workloads, launches, reps=20):
         ring_fused(i)
         sa.dit_attn_fwd_kvlen(q, k_txt, v_txt, txt_len, o=o_acc, lse=lse_acc, scale=rw.scale, merge=True)
 
-    us_j = time_graph(torch, ring_joint, passes, replays=2)
-    fl_joint = 4 * rw.B * rw.H * rw.Sq * (rw.Skv + 300) * rw.D
-    res["attn_joint_text_image_ring_e2e"] = attn_roofline(
-        "joint_e2e", fl_joint, us_j,
-        note="ring of 4 image chunks (fused hops) + 300 valid of 512 text keys merged once; "
-             "FLOP counts valid keys only")
+    if want("attn_joint_text_image_ring_e2e"):
+        us_j = time_graph(torch, ring_joint, passes, replays=2)
+        fl_joint = 4 * rw.B * rw.H * rw.Sq * (rw.Skv + 300) * rw.D
+        res["attn_joint_text_image_ring_e2e"] = attn_roofline(
+            "joint_e2e", fl_joint, us_j,
+            note="ring of 4 image chunks (fused hops) + 300 valid of 512 text keys merged once; "
+                 "FLOP counts valid keys only")
     del k_txt, v_txt
-    fn = lambda i: sa.dit_attn_fwd(q, kc[i % rw.R], vc[i % rw.R], o=o_part, lse=lse_part, scale=rw.scale,
-                                   workspace=ws_c)
-    avg = time_graph(torch, fn, launches)
-    med, mn = time_events(torch, fn, reps)
-    res["attn_ring_chunk"] = attn_roofline("ring_chunk", fl // rw.R, avg, med, mn)
-    fn = lambda i: sa.dit_attn_fwd_merge(q, kc[1 + i % 3], vc[1 + i % 3], o_acc, lse_acc, scale=rw.scale,
-                                         workspace=ws_m)
-    avg = time_graph(torch, fn, launches)
-    res["attn_ring_fused_hop"] = attn_roofline("ring_fused_hop", fl // rw.R, avg,
-                                               note="one dit_attn_fwd_merge hop at the chunk shape")
-    fn = lambda i: sa.dit_attn_fwd(q, k, v, o=o_acc, lse=lse_acc, scale=rw.scale, workspace=ws_u)
-    avg = time_graph(torch, fn, max(4, launches // 4))
-    med, mn = time_events(torch, fn, max(5, reps // 4))
-    res["attn_ring_unchunked"] = attn_roofline("ring_unchunked", fl, avg, med, mn)
-    res["ring_chunking_ratio"] = {
-        "fused_e2e_over_unchunked": round(us_f / avg, 4),
-        "chunked_e2e_over_unchunked": round(us / avg, 4)}
+    if want("attn_ring_chunk"):
+        fn = lambda i: sa.dit_attn_fwd(q, kc[i % rw.R], vc[i % rw.R], o=o_part, lse=lse_part, scale=rw.scale,
+                                       workspace=ws_c)
+        avg = time_graph(torch, fn, launches)
+        med, mn = time_events(torch, fn, reps)
+        res["attn_ring_chunk"] = attn_roofline("ring_chunk", fl // rw.R, avg, med, mn)
+    if want("attn_ring_fused_hop"):
+        fn = lambda i: sa.dit_attn_fwd_merge(q, kc[1 + i % 3], vc[1 + i % 3], o_acc, lse_acc, scale=rw.scale,
+                                             workspace=ws_m)
+        avg = time_graph(torch, fn, launches)
+        res["attn_ring_fused_hop"] = attn_roofline("ring_fused_hop", fl // rw.R, avg,
+                                                   note="one dit_attn_fwd_merge hop at the chunk shape")
+    if want("attn_ring_unchunked"):
+        fn = lambda i: sa.dit_attn_fwd(q, k, v, o=o_acc, lse=lse_acc, scale=rw.scale, workspace=ws_u)
+        avg = time_graph(torch, fn, max(4, launches // 4))
+        med, mn = time_events(torch, fn, max(5, reps // 4))
+        res["attn_ring_unchunked"] = attn_roofline("ring_unchunked", fl, avg, med, mn)
+        if us is not None and us_f is not None:
+            res["ring_chunking_ratio"] = {
+                "fused_e2e_over_unchunked": round(us_f / avg, 4),
+                "chunked_e2e_over_unchunked": round(us / avg, 4)}
     del q, k, v, o_acc, o_part, kc, vc
+
+
+def qwen_permutes(torch, sa, workloads, launches, want, res):
 
     # Qwen Ulysses QKV pack / unpack at U=4 (sequence pad) and U=5 (head pad),
     # on the rank that holds the pad rows / pad head, buffers rotated
     for name in ("qwen_u4", "qwen_u5"):
+        if not (want(f"{name}_pack_qkv") or want(f"{name}_unpack_qkv")):
+            continue
         w = workloads.WORKLOADS[name]
         L = sa.dit_a2a_layout_init(w.B, w.S, w.H_total, w.D, w.U, 1, 3)
         rank = w.U - 1
@@ -391,7 +460,7 @@ def attention_configs(torch, sa, workloads, launches, reps=20):
         real_rows = min(L.S_loc, w.S - rank * L.S_loc)
         pack_bytes = 2 * (3 * w.B * real_rows * w.H_total * w.D + send_elems)
         unpack_bytes = 2 * (send_elems + 3 * out_elems)
-        sets = rot_sets(pack_bytes + unpack_bytes)
+        sets = rot_sets(min(pack_bytes, unpack_bytes))   # each leg touches half of a set
         bufs = []
         for _ in range(sets):
             shard = [torch.empty((w.B, L.S_loc, w.H_total, w.D), dtype=torch.bfloat16, device="cuda").normal_()
@@ -406,7 +475,6 @@ def attention_configs(torch, sa, workloads, launches, reps=20):
                                                                out=bufs[i % sets][2]), launches)
         res[f"{name}_unpack_qkv"] = hbm_entry(unpack_bytes, us, rank=rank, sets=sets)
         del bufs
-    return res
 
 
 # ---------------------------------------------------------------------------
@@ -483,7 +551,7 @@ def side_measurements(torch, sa, workloads, launches):
     Lp = sa.dit_a2a_layout_init(1, S_u, H_u, D_u, U_u, 1, 3)
     r_rows, _ = Lu.counts()
     real = {"pack": 2 * 3 * r_rows[0] * H_u * D_u * 2, "unpack": 2 * 3 * S_u * (H_u // U_u) * D_u * 2}
-    sets = rot_sets(2 * real["pack"] + 2 * real["unpack"])
+    sets = rot_sets(min(real.values()))   # each leg touches its own buffers only
     bufs = []
     for _ in range(sets):
         shard_u = [torch.empty((1, r_rows[0], H_u, D_u), dtype=bf16, device="cuda").normal_() for _ in range(3)]
@@ -529,7 +597,7 @@ def side_measurements(torch, sa, workloads, launches):
     st1 = sa.dit_a2a_fp8_bytes_per_peer(L1, sa.DIT_HEAD_TO_SEQ)
     shard_b = fw.B * L3.S_loc * fw.H_total * fw.D * 2
     head_b = fw.B * fw.S * L3.H_loc * fw.D * 2
-    sets = rot_sets(3 * shard_b + 3 * head_b + fw.U * (st3 + st1))
+    sets = rot_sets(head_b + shard_b + fw.U * st1)   # the smallest leg's own bytes
     bufs = []
     for _ in range(sets):
         shard = [torch.empty((fw.B, L3.S_loc, fw.H_total, fw.D), dtype=bf16, device="cuda").normal_()
@@ -799,6 +867,11 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.only:
+        only = set(args.only.split(","))
+        res = attention_configs(torch, sa, workloads, args.graph_launches, only=only)
+        print(json.dumps({"configs": res}), flush=True)
+        return
     w = workloads.WORKLOADS[args.workload]
     one = Step(w, torch, sa, workloads, seed=0)
     n_sets = rot_sets(one.bytes())
@@ -827,11 +900,17 @@ def main():
     # the same K steps replayed from one captured graph
     steps_graph_us = time_graph(torch, lambda i: steps[i % n_sets].run(sa, rank), args.steps, replays=2)
 
-    # per-kernel average launch duration (graph replay over the rotated sets)
-    per_kernel = {}
+    # per-kernel average launch duration: graph replay, each kernel over
+    # buffer sets of its own, rotated beyond the Infinity Cache
+    per_kernel, sets_used = {}, {}
+    make, kb_all = kernel_pools(w, torch, sa, one, rank)
     for n in Step.NAMES + Step.UNFUSED:
-        per_kernel[n] = time_graph(torch, lambda i, n=n: steps[i % n_sets].run(sa, rank, only=n),
-                                   args.graph_launches)
+        alloc, call = make[n]
+        k_sets = rot_sets(kb_all[n])
+        bufs = [alloc() for _ in range(k_sets)]
+        per_kernel[n] = time_graph(torch, lambda i: call(bufs[i % k_sets]), max(args.graph_launches, k_sets))
+        sets_used[n] = k_sets
+        del bufs
     attn_us = per_kernel["BD_attention_send"]
     progress("per-kernel graph timings done")
     attn_flop = w.attn_flop()
@@ -840,10 +919,10 @@ def main():
     kernels = {}
     for n in Step.NAMES + Step.UNFUSED:
         if n in kb:
-            kernels[n] = hbm_entry(kb[n], per_kernel[n])
+            kernels[n] = hbm_entry(kb[n], per_kernel[n], sets=sets_used[n])
         else:
             kernels[n] = {"us": round(per_kernel[n], 2), "flop": attn_flop,
-                          "TFLOP/s": round(attn_flop / per_kernel[n] / 1e6, 1)}
+                          "TFLOP/s": round(attn_flop / per_kernel[n] / 1e6, 1), "sets": sets_used[n]}
     kernels["BD_attention_send"]["note"] = "attention storing O into the send buffer (replaces B + D)"
     kernels["unfused_B_plus_D_us"] = round(per_kernel["B_attention"] + per_kernel["D_pack_o"], 2)
 

@@ -534,10 +534,12 @@ dit_status_t dit_attn_fwd_kvlen(const void* q, const void* k, const void* v, con
  * multiplied, so its O may hold anything); both empty -> (0, -inf).
  * Math in fp32.
  *
- * o_acc, o_part: [B, Sq, H, D] in o_dtype (DIT_BF16 or DIT_F32);
- * lse_acc, lse_part: [B, H, Sq] fp32.  o_acc / lse_acc are read and
- * written in place; they must not overlap the part tensors.
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (dtype, alignment), HIP.
+ * o_acc, o_part: [B, Sq, H, D] in o_dtype (DIT_BF16 or DIT_F32), D one of
+ * 8, 16, 32, ..., 512; lse_acc, lse_part: [B, H, Sq] fp32.  o_acc / lse_acc
+ * are read and written in place; they must not overlap the part tensors.
+ * Errors: INVALID_ARGUMENT (negative sizes, NULL pointers, overlap),
+ * UNSUPPORTED (dtype, head size, alignment, 2^31 or more 8-element chunks),
+ * HIP.
  */
 dit_status_t dit_attn_merge(void* o_acc, float* lse_acc, const void* o_part,
                             const float* lse_part, int32_t B, int32_t Sq, int32_t H, int32_t D,

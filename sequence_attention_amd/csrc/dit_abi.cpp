@@ -894,7 +894,7 @@ dit_status_t dit_attn_merge(void* o_acc, float* lse_acc, const void* o_part, con
   if (o_dtype == DIT_F16) return fail(DIT_ERR_UNSUPPORTED, "fp16 merge is not served");
   // one row's D/8 lanes must sit in one wavefront (the row's LSE is updated
   // in place after all of them read it)
-  if (D % 8 != 0 || D / 8 > 64 || ((D / 8) & (D / 8 - 1)) != 0)
+  if (D < 8 || D % 8 != 0 || D / 8 > 64 || ((D / 8) & (D / 8 - 1)) != 0)
     return fail(DIT_ERR_UNSUPPORTED, "head dim %d: merge needs D = 8 * 2^k <= 512", D);
   const int64_t rows = (int64_t)B * Sq * H;
   if (rows == 0) {

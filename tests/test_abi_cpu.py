@@ -360,7 +360,7 @@ def _merge(lib, oa=A, la=A + 2**24, op=A + 2**25, lp=A + 2**26, B=1, Sq=16, H=2,
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), INV), (dict(D=-8), INV), (dict(dt=9), INV), (dict(dt=1), UNS),
-    (dict(D=96), UNS), (dict(D=12), UNS), (dict(D=1024), UNS),
+    (dict(D=96), UNS), (dict(D=12), UNS), (dict(D=1024), UNS), (dict(D=0), UNS),
     (dict(oa=0), INV), (dict(lp=0), INV),
     (dict(oa=A + 8), UNS), (dict(la=A + 2**24 + 2), UNS),
     (dict(op=A + 256), INV), (dict(lp=A + 2**24 + 4), INV),

@@ -21,7 +21,8 @@ def _partials(B, Sq, H, D, dtype, seed):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("shape", [(1, 256, 4, 64), (2, 7145, 6, 128), (1, 33, 3, 128)])
+@pytest.mark.parametrize("shape", [(1, 256, 4, 64), (2, 7145, 6, 128), (1, 33, 3, 128), (1, 300, 3, 8),
+                                   (2, 37, 2, 16), (1, 70, 2, 32), (1, 45, 2, 256), (1, 21, 2, 512)])
 def test_merge_matches_oracle(dtype, shape):
     log(f"merge {dtype} {shape}")
     oa, la = _partials(*shape, dtype, 1)
