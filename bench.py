@@ -66,7 +66,14 @@ CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches 
 # for the kernel source they were taken on (SHA-256 below): any change to
 # that file reports traffic as null until the counters are taken again.
 ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
-ATTN_TRAFFIC = {"src_sha256": None, "per_shape": {}}
+ATTN_TRAFFIC = {
+    "src_sha256": "c7db640208c349f8fabb6930e5d2fcab22656e02110787f3fe023b8127e8daa0",
+    # shape: (read bytes, write bytes) per launch
+    "per_shape": {"flux": (52_257_792, 14_378_394), "qwen_u4": (151_028_941, 55_758_336),
+                  "qwen_u5": (132_957_389, 45_326_950), "wan": (2_109_925_171, 98_289_766),
+                  "ring_chunk": (111_803_597, 61_230_694), "ring_unchunked": (262_809_190, 61_251_584),
+                  "ring_fused_hop": (137_358_336, 66_365_338)},
+}
 
 
 def parse():
@@ -85,8 +92,8 @@ def parse():
     ap.add_argument("--graph-launches", type=int, default=20,
                     help="launches captured per graph for the kernel timings")
     ap.add_argument("--only", metavar="NAMES",
-                    help="comma-separated entries of `configs` to run alone (no step, no other part); "
-                         "for profiling one shape per run")
+                    help="comma-separated parts to run alone, for profiling one measurement per run: "
+                         "'kernels' (the step's per-kernel timings), 'side', or entries of `configs`")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print the per-kernel table of a rocprofv3 kernel-trace database and exit")
     ap.add_argument("--pmc-summary", metavar="CSV",
@@ -290,6 +297,31 @@ def kernel_pools(w, torch, sa, step, rank):
                      lambda b: sa.dit_ulysses_pack(L1, H2S, rank, b[0], send=b[1])),
     }
     return make, kb
+
+
+def kernel_timings(w, torch, sa, workloads, step, rank, launches):
+    """Average launch duration of each launch of the step (and of the
+    unfused pair BD replaces): graph replay, each kernel over buffer sets of
+    its own, rotated beyond the Infinity Cache.  Returns the `kernels`
+    entries and the attention's average launch duration."""
+    make, kb_all = kernel_pools(w, torch, sa, step, rank)
+    kb = kernel_bytes(step)
+    attn_flop = w.attn_flop()
+    kernels, per_kernel = {}, {}
+    for n in Step.NAMES + Step.UNFUSED:
+        alloc, call = make[n]
+        k_sets = rot_sets(kb_all[n])
+        bufs = [alloc() for _ in range(k_sets)]
+        per_kernel[n] = time_graph(torch, lambda i: call(bufs[i % k_sets]), max(launches, k_sets))
+        del bufs
+        if n in kb:
+            kernels[n] = hbm_entry(kb[n], per_kernel[n], sets=k_sets)
+        else:
+            kernels[n] = {"us": round(per_kernel[n], 2), "flop": attn_flop,
+                          "TFLOP/s": round(attn_flop / per_kernel[n] / 1e6, 1), "sets": k_sets}
+    kernels["BD_attention_send"]["note"] = "attention storing O into the send buffer (replaces B + D)"
+    kernels["unfused_B_plus_D_us"] = round(per_kernel["B_attention"] + per_kernel["D_pack_o"], 2)
+    return kernels, per_kernel["BD_attention_send"]
 
 
 def kernel_bytes(step):
@@ -867,12 +899,20 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    w = workloads.WORKLOADS[args.workload]
     if args.only:
         only = set(args.only.split(","))
-        res = attention_configs(torch, sa, workloads, args.graph_launches, only=only)
-        print(json.dumps({"configs": res}), flush=True)
+        out = {}
+        if "kernels" in only:
+            out["kernels"] = kernel_timings(w, torch, sa, workloads, Step(w, torch, sa, workloads, seed=0), 0,
+                                            args.graph_launches)[0]
+        if "side" in only:
+            out["side"] = side_measurements(torch, sa, workloads, args.graph_launches)
+        rest = only - {"kernels", "side"}
+        if rest:
+            out["configs"] = attention_configs(torch, sa, workloads, args.graph_launches, only=rest)
+        print(json.dumps(out), flush=True)
         return
-    w = workloads.WORKLOADS[args.workload]
     one = Step(w, torch, sa, workloads, seed=0)
     n_sets = rot_sets(one.bytes())
     steps = [one] + [Step(w, torch, sa, workloads, seed=i) for i in range(1, n_sets)]
@@ -900,31 +940,10 @@ def main():
     # the same K steps replayed from one captured graph
     steps_graph_us = time_graph(torch, lambda i: steps[i % n_sets].run(sa, rank), args.steps, replays=2)
 
-    # per-kernel average launch duration: graph replay, each kernel over
-    # buffer sets of its own, rotated beyond the Infinity Cache
-    per_kernel, sets_used = {}, {}
-    make, kb_all = kernel_pools(w, torch, sa, one, rank)
-    for n in Step.NAMES + Step.UNFUSED:
-        alloc, call = make[n]
-        k_sets = rot_sets(kb_all[n])
-        bufs = [alloc() for _ in range(k_sets)]
-        per_kernel[n] = time_graph(torch, lambda i: call(bufs[i % k_sets]), max(args.graph_launches, k_sets))
-        sets_used[n] = k_sets
-        del bufs
-    attn_us = per_kernel["BD_attention_send"]
+    kernels, attn_us = kernel_timings(w, torch, sa, workloads, one, rank, args.graph_launches)
     progress("per-kernel graph timings done")
     attn_flop = w.attn_flop()
     value = attn_flop / (ms_per_step * 1e-3) / 1e12
-    kb = kernel_bytes(one)
-    kernels = {}
-    for n in Step.NAMES + Step.UNFUSED:
-        if n in kb:
-            kernels[n] = hbm_entry(kb[n], per_kernel[n], sets=sets_used[n])
-        else:
-            kernels[n] = {"us": round(per_kernel[n], 2), "flop": attn_flop,
-                          "TFLOP/s": round(attn_flop / per_kernel[n] / 1e6, 1), "sets": sets_used[n]}
-    kernels["BD_attention_send"]["note"] = "attention storing O into the send buffer (replaces B + D)"
-    kernels["unfused_B_plus_D_us"] = round(per_kernel["B_attention"] + per_kernel["D_pack_o"], 2)
 
     result = {
         "metric": METRIC,
