@@ -67,12 +67,12 @@ CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches 
 # that file reports traffic as null until the counters are taken again.
 ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
 ATTN_TRAFFIC = {
-    "src_sha256": "c7db640208c349f8fabb6930e5d2fcab22656e02110787f3fe023b8127e8daa0",
+    "src_sha256": "1cf84a4037ac7c4c1630d39b99306172f61c433bd854791c080af8e564ba7593",
     # shape: (read bytes, write bytes) per launch
-    "per_shape": {"flux": (52_257_792, 14_378_394), "qwen_u4": (151_028_941, 55_758_336),
-                  "qwen_u5": (132_957_389, 45_326_950), "wan": (2_109_925_171, 98_289_766),
-                  "ring_chunk": (111_803_597, 61_230_694), "ring_unchunked": (262_809_190, 61_251_584),
-                  "ring_fused_hop": (137_358_336, 66_365_338)},
+    "per_shape": {"flux": (52_190_208, 14_389_453), "qwen_u4": (151_080_141, 55_775_846),
+                  "qwen_u5": (133_014_323, 45_349_683), "wan": (2_109_966_131, 98_287_309),
+                  "ring_chunk": (111_775_949, 61_270_323), "ring_unchunked": (262_731_366, 61_276_262),
+                  "ring_fused_hop": (137_284_813, 65_854_976)},
 }
 
 

@@ -256,8 +256,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       // bytes of this batch's keys from the block start, none for a block
       // past kb1: loads beyond them are out of range, access no memory and
       // fill their LDS bytes with zeros (finite; those scores are masked)
-      const int64_t avail = kb < kb1 ? (int64_t)(skv - j0) * (int64_t)rs * 2 : 0;
-      const int nrec = (int)min(avail, (int64_t)0x7fffffff);
+      // (a scalar select, not a branch: the QK products and the weights stay
+      // in one scheduling region)
+      const uint32_t rows = kb < kb1 ? (uint32_t)max(skv - j0, 0) : 0u;
+      const int nrec = (int)min((uint64_t)rows * (uint64_t)(rs * 2), (uint64_t)0x7fffffff);
       const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb_ptr, (short)0, nrec, kBufferWord3);
       const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb_ptr, (short)0, nrec, kBufferWord3);
 #pragma unroll
