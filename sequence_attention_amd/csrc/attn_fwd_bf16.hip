@@ -122,16 +122,20 @@ __device__ __forceinline__ uint32_t logical_wg(uint32_t bid, uint32_t n) {
 }
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row of K or V.
-// D = 128 (16 chunks, 256-byte rows): a bit permutation of r mod 16, so the
-//   32 rows of an A-operand read (same logical chunk) hit 16 distinct chunk
-//   positions per half wave, and the 4 rows of a transpose read land their
-//   two chunks on 8 distinct positions.
-// D = 64 (8 chunks, 128-byte rows, two rows per bank line): the same two
-//   properties with the row parity taking one bank half.
+// gfx950's LDS serves 64 banks x 4 bytes per cycle: 16 lanes of a 16-byte
+// read (the K operand) or 32 lanes of an 8-byte read (the V^T transpose
+// read) per cycle.  The swizzle depends on r mod 16 only and keeps both
+// conflict-free, also under a 32-bank reading (8 / 16 lanes per cycle):
+//   K: any 16 aligned rows, same logical chunk, land on distinct banks;
+//   V^T: 4 aligned rows x 4 consecutive logical chunks (D = 128; two rows
+//   share a 256-byte bank line at D = 64) land on distinct banks.
+// With r = (r3 r2 r1 r0): D = 128: (r1^r3, r0, r1, r2); D = 64: (r1, r0^r3, r2).
+// (The counter SQ_LDS_BANK_CONFLICT reads 0 for both head sizes.)
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
-  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+  if constexpr (D == 128) return ((r1 ^ r3) << 3) | (r0 << 2) | (r1 << 1) | r2;
+  else return (r1 << 2) | ((r0 ^ r3) << 1) | r2;
 }
 
 // s_waitcnt with vmcnt(n), other counters untouched (gfx9 encoding).
