@@ -15,14 +15,16 @@
 //  * Keys are consumed in blocks of 64.  K and V blocks go from L2 straight
 //    into LDS with buffer_load_dwordx4 ... lds (no VGPR staging; the
 //    per-block address is a scalar buffer base, so no VALU either) through a
-//    4-stage ring: loads run three blocks ahead of the multiply, which hides
-//    L2 / HBM latency; one barrier per block.  The address range of each
-//    block's buffer descriptor ends at the last valid key (and is empty for
-//    a block past the workgroup's range), so tail rows and the look-ahead
-//    past the end are out-of-range loads that touch no memory: the block
-//    loop issues and waits the same way every time, without branches.  Rows are stored with an XOR
-//    swizzle of their 16-byte chunks, chosen so that both operand reads
-//    below are bank-conflict free.
+//    4-stage ring: after the barrier of block kb, block kb + 2 is issued
+//    into the stage of block kb - 2, so two blocks are in flight while one
+//    is multiplied (measured slightly faster than three ahead); one barrier
+//    per block.  The address range of each block's buffer descriptor ends
+//    at the last valid key (and is empty for a block past the workgroup's
+//    range), so tail rows and the look-ahead past the end are out-of-range
+//    loads that touch no memory: the block loop issues and waits the same
+//    way every time, without branches.  Rows are stored with an XOR swizzle
+//    of their 16-byte chunks, chosen so that both operand reads below are
+//    bank-conflict free.
 //  * Both products use v_mfma_f32_32x32x16_bf16 in a transposed orientation:
 //    S^T = K Q^T and O^T = V^T P^T.  The S^T accumulator gives each lane one
 //    query and 16 keys, so the row max needs one swap with the partner lane
@@ -284,22 +286,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     float lsum = 0.0f;         // this lane's share of the row sum (for LSE)
     float lsum_r = 0.0f;       // ... of the bf16-rounded weights (normalises O)
 
-    // one key block from stage ST; block kb + 3 is streamed into stage ST - 1
-    // one key block from stage ST; kMask: the block reaches past skv
+    // one key block from stage ST; block kb + 2 is streamed into stage
+    // ST + 2 (block kb - 2's); kMask: the block reaches past skv
     auto block = [&](auto stage, int kb, auto masked) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage)::value;
       constexpr bool kMask = decltype(masked)::value;
       const int j0 = kb * kBN;
-      // this wave's loads of block kb have landed once only those of blocks
-      // kb + 1 and kb + 2 are outstanding (always issued, past kb1 empty)
-      wait_vmcnt<2 * LPB>();
+      // this wave's loads of block kb have landed once only those of block
+      // kb + 1 are outstanding (always issued, past kb1 empty)
+      wait_vmcnt<LPB>();
       // Workgroup barrier without __syncthreads()'s release fence, which
       // would wait for every outstanding load (vmcnt(0)) and drain the ring.
       // LDS reads of the stage being recycled completed before their MFMAs
       // issued; the empty asm statements keep the compiler from moving
       // memory accesses across the barrier.
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();  // everyone's loads of block kb landed; stage ST - 1 is free
+      __builtin_amdgcn_s_barrier();  // everyone's loads of block kb landed; stage ST + 2 is free
       asm volatile("" ::: "memory");
       const char* ks = ST == 0 ? k_s0 : ST == 1 ? k_s1 : ST == 2 ? k_s2 : k_s3;
       const char* vs = ST == 0 ? v_s0 : ST == 1 ? v_s1 : ST == 2 ? v_s2 : v_s3;
@@ -326,14 +328,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      // Stream block kb + 3 into the free stage.  Issued here, after the QK
+      // Stream block kb + 2 into the free stage.  Issued here, after the QK
       // products rather than right after the barrier, so that the eight
       // waves' loads do not all queue at once in front of their first LDS
       // reads (measured 2-3 % faster).
-      if constexpr (ST == 0) issue(kb + 3, k_s3, v_s3);
-      else if constexpr (ST == 1) issue(kb + 3, k_s0, v_s0);
-      else if constexpr (ST == 2) issue(kb + 3, k_s1, v_s1);
-      else issue(kb + 3, k_s2, v_s2);
+      if constexpr (ST == 0) issue(kb + 2, k_s2, v_s2);
+      else if constexpr (ST == 1) issue(kb + 2, k_s3, v_s3);
+      else if constexpr (ST == 2) issue(kb + 2, k_s0, v_s0);
+      else issue(kb + 2, k_s1, v_s1);
       // lane holds S^T[key = 32t + 8(r/4) + 4g + r%4][query l32]
       if constexpr (kMask) {
 #pragma unroll
@@ -452,7 +454,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     }
     issue(kb0, k_s0, v_s0);
     issue(kb0 + 1, k_s1, v_s1);
-    issue(kb0 + 2, k_s2, v_s2);
     // Blocks wholly inside the key range need no mask; the partial last
     // block (present when kb1 reaches past skv rounded down) is peeled off.
     // Stage of block x: (x - kb0) mod 4.
