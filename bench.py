@@ -67,12 +67,12 @@ CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches 
 # that file reports traffic as null until the counters are taken again.
 ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
 ATTN_TRAFFIC = {
-    "src_sha256": "1cf84a4037ac7c4c1630d39b99306172f61c433bd854791c080af8e564ba7593",
+    "src_sha256": "b3ef17fdc33795ee17b99ce306f1290393798028424dd4f490b320988c10857f",
     # shape: (read bytes, write bytes) per launch
-    "per_shape": {"flux": (52_190_208, 14_389_453), "qwen_u4": (151_080_141, 55_775_846),
-                  "qwen_u5": (133_014_323, 45_349_683), "wan": (2_109_966_131, 98_287_309),
-                  "ring_chunk": (111_775_949, 61_270_323), "ring_unchunked": (262_731_366, 61_276_262),
-                  "ring_fused_hop": (137_284_813, 65_854_976)},
+    "per_shape": {"flux": (52_184_064, 14_378_496), "qwen_u4": (151_094_682, 55_741_235),
+                  "qwen_u5": (133_024_154, 45_326_131), "wan": (2_110_191_002, 98_287_206),
+                  "ring_chunk": (111_767_757, 61_251_584), "ring_unchunked": (262_763_315, 61_268_685),
+                  "ring_fused_hop": (137_265_152, 65_973_146)},
 }
 
 
