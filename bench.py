@@ -7,12 +7,13 @@ batch of synthetic input, the FLUX.1-like 1024x1024 shard by default
 Ulysses degree 2, ring degree 1):
 
   A1  QKV sequence-to-head pack   [1,2304,24,128] x3 -> [2,3,1,2304,12,128]
-  A3  QKV unpack                  (the send buffer stands in for the received
-                                   one: same bytes and shape; the all-to-all
-                                   itself is a collective, outside this path)
-  BD  attention with LSE, O stored straight into the head-to-sequence send
-      buffer [1,4608,12,128] -> [2,1,1,2304,12,128]; ring degree 1, so the
-      hop loop is one chunk and no merge (B and D of the method in one kernel)
+  ABD attention with LSE reading Q, K, V straight from the receive buffer
+      [2,3,1,2304,12,128] (the send buffer stands in for the received one:
+      same bytes and shape; the all-to-all itself is a collective, outside
+      this path) and storing O straight into the head-to-sequence send
+      buffer [2,1,1,2304,12,128]; ring degree 1, so the hop loop is one chunk
+      and no merge (the unpack A3, attention B and pack D of the method in
+      one kernel; the unfused launches are timed beside it)
   E   O unpack                    -> [1,2304,24,128]
   F   CFG combine                 [2,4096,64] fp32 latent prediction, g = 4
 
@@ -206,8 +207,10 @@ def attn_roofline(shape_name, flop, avg_us, ev_median=None, ev_min=None, **extra
 class Step:
     """Buffers and launches of one rank's hot-path step (one input set)."""
 
-    NAMES = ("A1_pack_qkv", "A3_unpack_qkv", "BD_attention_send", "E_unpack_o", "F_cfg")
-    UNFUSED = ("B_attention", "D_pack_o")   # the two launches BD replaces
+    NAMES = ("A1_pack_qkv", "ABD_attention_a2a", "E_unpack_o", "F_cfg")
+    # the launches ABD replaces: the unpack A3 and attention into the send
+    # buffer BD, which itself replaces attention B and the pack D
+    UNFUSED = ("A3_unpack_qkv", "BD_attention_send", "B_attention", "D_pack_o")
 
     def __init__(self, w, torch, sa, workloads, seed):
         dev = "cuda"
@@ -245,6 +248,8 @@ class Step:
         launches = {
             "A1_pack_qkv": lambda: sa.dit_ulysses_pack(self.L3, S2H, rank, self.shard, send=self.send3),
             "A3_unpack_qkv": lambda: sa.dit_ulysses_unpack(self.L3, S2H, rank, self.send3, out=self.qkv),
+            "ABD_attention_a2a": lambda: sa.dit_attn_fwd_a2a(self.send3, self.L3, rank, send=self.send1,
+                                                             lse=self.lse, scale=w.scale, workspace=self.ws),
             "BD_attention_send": lambda: sa.dit_attn_fwd_send(*self.qkv, self.L1, rank, send=self.send1,
                                                               lse=self.lse, scale=w.scale, workspace=self.ws),
             "E_unpack_o": lambda: sa.dit_ulysses_unpack(self.L1, H2S, rank, self.send1, out=[self.out]),
@@ -270,6 +275,7 @@ def kernel_pools(w, torch, sa, step, rank):
     kb = kernel_bytes(step)
     o_b = w.B * w.S * L3.H_loc * w.D * 2
     kb["BD_attention_send"] = 3 * o_b + kb["D_pack_o"] - o_b
+    kb["ABD_attention_a2a"] = w.U * L3.elems_per_peer * 2 + kb["D_pack_o"] - o_b
     kb["B_attention"] = 4 * o_b
     shard = lambda: [torch.empty((w.B, L3.S_loc, w.H_total, w.D), dtype=bf16, device=dev).normal_()
                      for _ in range(3)]
@@ -284,6 +290,9 @@ def kernel_pools(w, torch, sa, step, rank):
                         lambda b: sa.dit_ulysses_pack(L3, S2H, rank, b[0], send=b[1])),
         "A3_unpack_qkv": (lambda: (send3(), heads(3)),
                           lambda b: sa.dit_ulysses_unpack(L3, S2H, rank, b[0], out=b[1])),
+        "ABD_attention_a2a": (lambda: (send3(), send1(), lse()),
+                              lambda b: sa.dit_attn_fwd_a2a(b[0], L3, rank, send=b[1], lse=b[2], scale=w.scale,
+                                                            workspace=step.ws)),
         "BD_attention_send": (lambda: (heads(3), send1(), lse()),
                               lambda b: sa.dit_attn_fwd_send(*b[0], L1, rank, send=b[1], lse=b[2], scale=w.scale,
                                                              workspace=step.ws)),
@@ -319,9 +328,12 @@ def kernel_timings(w, torch, sa, workloads, step, rank, launches):
         else:
             kernels[n] = {"us": round(per_kernel[n], 2), "flop": attn_flop,
                           "TFLOP/s": round(attn_flop / per_kernel[n] / 1e6, 1), "sets": k_sets}
+    kernels["ABD_attention_a2a"]["note"] = ("attention reading Q, K, V from the receive buffer and storing O "
+                                            "into the send buffer (replaces A3 + BD)")
     kernels["BD_attention_send"]["note"] = "attention storing O into the send buffer (replaces B + D)"
+    kernels["unfused_A3_plus_BD_us"] = round(per_kernel["A3_unpack_qkv"] + per_kernel["BD_attention_send"], 2)
     kernels["unfused_B_plus_D_us"] = round(per_kernel["B_attention"] + per_kernel["D_pack_o"], 2)
-    return kernels, per_kernel["BD_attention_send"]
+    return kernels, per_kernel["ABD_attention_a2a"]
 
 
 def kernel_bytes(step):
@@ -968,8 +980,8 @@ def main():
                                     "s_memrealtime (100 MHz) ticks per workgroup, 256 workgroups, "
                                     "median / min / max; fma = light load, mfma = bf16 MFMA load"},
         "ms_per_step_graph": round(steps_graph_us / 1e3, 4),
-        "roofline": attn_roofline(w.name, attn_flop, attn_us,
-                                  kernel="attn_bf16_kernel<128, false, false> (dit_attn_fwd_send)"),
+        "roofline": attn_roofline(w.name + "_a2a", attn_flop, attn_us,
+                                  kernel="attn_bf16_kernel<128, false, false, true> (dit_attn_fwd_a2a)"),
         "kernels": kernels,
     }
     result["roofline"].pop("flop", None)

@@ -19,6 +19,9 @@
  *                                          exchanged as FP8 (K kept bf16)
  *   dit_attn_fwd_send                      attention that stores O straight into
  *                                          the head-to-sequence send buffer
+ *   dit_attn_fwd_a2a                       ... that also reads Q, K and V
+ *                                          straight from the sequence-to-head
+ *                                          receive buffer
  *   dit_attn_fwd, dit_attn_fwd_ws          attention with per-row LSE (_ws:
  *                                          with a caller workspace that lets
  *                                          the kernel split the last round)
@@ -476,6 +479,41 @@ dit_status_t dit_attn_fwd_ws(const void* q, const void* k, const void* v, void* 
 dit_status_t dit_attn_fwd_send(const void* q, const void* k, const void* v, void* send_buf,
                                float* lse, const dit_a2a_layout* layout, int32_t rank, int32_t Skv,
                                float scale, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Attention of Ulysses rank `rank` between the two all-to-alls: Q, K and V
+ * are read straight from the packed sequence-to-head receive buffer and O
+ * is stored straight into the head-to-sequence send buffer (edge-dit.cpp
+ * "Parallel execution", Ulysses section: receive-buffer decoding and plane
+ * extraction into the head-sharded layout before attention, and the packed
+ * head-to-sequence operator after it; here the attention kernel addresses
+ * both buffers itself, so neither the unpack nor the pack moves Q, K, V or
+ * O through HBM).  The result equals, bit for bit,
+ *   dit_ulysses_unpack(layout, DIT_SEQ_TO_HEAD, rank, recv_buf, {q, k, v})
+ *   followed by dit_attn_fwd_send(q, k, v, send_buf, lse, layout1, rank, S,
+ *   scale, workspace, workspace_bytes), with layout1 the same group with
+ *   n_planes = 1.
+ * Query and key row t of the sequence (t < S) are row t % S_loc of source
+ * peer t / S_loc's chunk of the receive buffer: Q, K, V[b, t, h', :] =
+ * recv[t / S_loc, plane 0 / 1 / 2, b, t % S_loc, h', :].  Pad rows (t >= S)
+ * are not attended to.
+ *
+ * layout: from dit_a2a_layout_init with n_planes = 3 and dtype DIT_BF16,
+ *   S_loc >= 64; B, S, H_loc and D of the call come from it.
+ * recv_buf: [U, 3, B, S_loc, H_loc, D] bf16 as received (16-byte aligned);
+ * send_buf: [U, 1, B, S_loc, H_loc, D] bf16, every element written
+ *   (pad rows and pad heads as 0); lse: [B, H_loc, S] fp32 or NULL.
+ * workspace, workspace_bytes: as dit_attn_fwd_ws (sized by
+ *   dit_attn_workspace_size(B, S, S, H_loc, D, BF16, BF16, 0, ...)).
+ * Uses no memory beyond its arguments.
+ * Errors: INVALID_ARGUMENT (as dit_ulysses_unpack for the layout and rank,
+ *   n_planes != 3, outputs or workspace overlapping the receive buffer, and
+ *   as dit_attn_fwd_ws for the other arguments); UNSUPPORTED (dtype not
+ *   bf16, S_loc < 64, alignment, size limits); HIP.
+ */
+dit_status_t dit_attn_fwd_a2a(const void* recv_buf, void* send_buf, float* lse,
+                              const dit_a2a_layout* layout, int32_t rank, float scale, void* workspace,
+                              int64_t workspace_bytes, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

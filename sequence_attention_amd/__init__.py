@@ -34,7 +34,7 @@ __all__ = [
     "dit_ulysses_unpack_uneven", "dit_ring_anything_pad", "dit_ring_anything_trim",
     "DitA2AUnevenLayout",
     "dit_a2a_fp8_bytes_per_peer", "dit_ulysses_pack_fp8", "dit_ulysses_unpack_fp8",
-    "dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_send", "dit_attn_fwd_noalloc", "dit_attn_workspace_size", "dit_attn_fwd_kvlen", "dit_attn_merge",
+    "dit_attn_fwd", "dit_attn_fwd_ws", "dit_attn_fwd_send", "dit_attn_fwd_a2a", "dit_attn_fwd_noalloc", "dit_attn_workspace_size", "dit_attn_fwd_kvlen", "dit_attn_merge",
     "dit_attn_fwd_merge", "dit_cfg_combine", "dit_clock_probe", "DitA2ALayout", "DitError",
     "DIT_BF16", "DIT_F16", "DIT_F32", "DIT_SEQ_TO_HEAD", "DIT_HEAD_TO_SEQ",
 ]
@@ -522,6 +522,45 @@ def dit_attn_fwd_send(q, k, v, layout: DitA2ALayout, rank: int, send=None, lse=N
     check(lib().dit_attn_fwd_send(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(send, "send"), lse_ptr,
                                   ctypes.byref(layout), rank, Skv, float(scale), ws_ptr, ws_bytes, st),
           "dit_attn_fwd_send")
+    return send, lse
+
+
+def dit_attn_fwd_a2a(recv, layout: DitA2ALayout, rank: int, send=None, lse=None, scale=None,
+                     want_lse=True, stream=None, workspace=True):
+    """Attention of Ulysses rank `rank` read straight from the packed
+    sequence-to-head receive buffer recv [U, 3, B, S_loc, H_loc, D] (planes
+    Q, K, V; bf16) and stored straight into the head-to-sequence send buffer
+    [U, 1, B, S_loc, H_loc, D]: equal, bit for bit, to dit_ulysses_unpack
+    (SEQ_TO_HEAD) followed by dit_attn_fwd_send.  layout has n_planes = 3,
+    dtype bf16 and S_loc >= 64.  Returns (send, LSE [B, H_loc, S] or None)."""
+    torch = _torch()
+    if layout.n_planes != 3 or layout.dtype != DIT_BF16:
+        raise ValueError("the receive layout must have n_planes = 3 and dtype bf16")
+    _expect(recv, "recv", layout.U * layout.elems_per_peer, torch.bfloat16)
+    dev = recv.device
+    B, S, H, D = layout.B, layout.S, layout.H_loc, layout.D
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    one = layout.U * (layout.elems_per_peer // 3)
+    if send is None:
+        send = torch.empty((layout.U, 1, B, layout.S_loc, H, D), dtype=torch.bfloat16, device=dev)
+    _expect(send, "send", one, torch.bfloat16, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _expect(lse, "lse", B * H * S, torch.float32, dev)
+    st = _stream(stream)
+    if workspace is True:
+        workspace = _workspace(dit_attn_workspace_size(B, S, S, H, D, DIT_BF16, DIT_BF16), dev, st)
+    elif workspace is False:
+        workspace = None
+    elif workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    ws_ptr, ws_bytes = (ctypes.c_void_p(0), 0) if workspace is None else (_dev(workspace, "workspace"),
+                                                                         workspace.numel())
+    lse_ptr = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
+    check(lib().dit_attn_fwd_a2a(_dev(recv, "recv"), _dev(send, "send"), lse_ptr, ctypes.byref(layout), rank,
+                                 float(scale), ws_ptr, ws_bytes, st), "dit_attn_fwd_a2a")
     return send, lse
 
 

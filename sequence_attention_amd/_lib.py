@@ -48,6 +48,7 @@ EXPORTS = (
     "dit_attn_workspace_size",
     "dit_attn_fwd_ws",
     "dit_attn_fwd_send",
+    "dit_attn_fwd_a2a",
     "dit_attn_fwd_noalloc",
     "dit_attn_fwd_kvlen",
     "dit_attn_merge",
@@ -168,6 +169,9 @@ def _declare(lib):
     lib.dit_attn_fwd_send.restype = ctypes.c_int
     lib.dit_attn_fwd_send.argtypes = [_P, _P, _P, _P, _P, ctypes.POINTER(DitA2ALayout), _I32, _I32,
                                       ctypes.c_float, _P, ctypes.c_int64, _P]
+    lib.dit_attn_fwd_a2a.restype = ctypes.c_int
+    lib.dit_attn_fwd_a2a.argtypes = [_P, _P, _P, ctypes.POINTER(DitA2ALayout), _I32, ctypes.c_float, _P,
+                                     ctypes.c_int64, _P]
     lib.dit_attn_fwd_noalloc.restype = ctypes.c_int
     lib.dit_attn_fwd_noalloc.argtypes = [_P, _P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                             ctypes.c_int, _P]

@@ -104,6 +104,14 @@ struct Params {
   int32_t send_rows;
   int32_t send_batches;
   int32_t o_heads;
+  // kRecv: Q, K and V are planes of the sequence-to-head receive buffer
+  // [U, 3, B, in_rows, H, D] (q, k, v point at planes 0, 1, 2 of peer 0's
+  // chunk; in_peer elements between peers): global row t is row t % in_rows
+  // of peer t / in_rows.
+  int32_t in_rows;
+  int32_t in_last_peer;  // U - 1
+  FastDiv in_div;        // division by in_rows
+  int64_t in_peer;
 };
 
 // Element offset of the first dim of query row q_row of batch b in O
@@ -155,7 +163,7 @@ constexpr size_t slot_floats() {
   return (size_t)kWaves * 64 * (D / 2 + 4);
 }
 
-template <int D, bool kOutF32, bool kMerge>
+template <int D, bool kOutF32, bool kMerge, bool kRecv>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   constexpr int ROWB = D * 2;                 // bytes of one K/V row
   constexpr int BLKB = kBN * ROWB;            // bytes of one K or V block
@@ -198,12 +206,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
   // byte offset is loop-invariant; rows past the last key are out of the
   // descriptor's range (read as zeros, their scores masked).
   uint32_t ld_off[INSTR_W];
+  int ld_row[INSTR_W];
 #pragma unroll
   for (int u = 0; u < INSTR_W; ++u) {
     const int off = (wave * INSTR_W + u) * 1024 + lane * 16;
     const int row = off / ROWB;
     const int col = (((off % ROWB) / 16) ^ swz<D>(row)) * 8;  // element column
     ld_off[u] = (uint32_t)(((size_t)row * rs + col) * 2);
+    ld_row[u] = row;
   }
 
   // ---- per-lane LDS read offsets ------------------------------------------
@@ -239,15 +249,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
     const int skv = p.kv_len != nullptr ? min(max(p.kv_len[b], 0), p.Skv) : p.Skv;
     const int kb1 = min(whole ? nblocks : (int)((uint64_t)(piece + 1) * nblocks / p.split),
                         (skv + kBN - 1) / kBN);
-    const uint16_t* kbase = p.k + (size_t)b * p.Skv * rs + (size_t)h * D;
-    const uint16_t* vbase = p.v + (size_t)b * p.Skv * rs + (size_t)h * D;
+    const size_t kv_batch = kRecv ? (size_t)p.in_rows : (size_t)p.Skv;  // rows between batches
+    const uint16_t* kbase = p.k + (size_t)b * kv_batch * rs + (size_t)h * D;
+    const uint16_t* vbase = p.v + (size_t)b * kv_batch * rs + (size_t)h * D;
 
     // ---- Q slice of this wave in registers: B operand of S^T = K Q^T -----
     const int q_row = qt * kBM + wave * 32 + l32;
     const bool q_ok = q_row < p.Sq;
     bf16x8 qf[KSTEPS];
     {
-      const uint16_t* qp = p.q + ((size_t)b * p.Sq + (q_ok ? q_row : 0)) * rs + (size_t)h * D + 8 * g;
+      const int qr = q_ok ? q_row : 0;
+      const uint16_t* qp;
+      if constexpr (kRecv) {
+        const uint32_t peer = fdiv((uint32_t)qr, p.in_div);
+        const int sr = qr - (int)peer * p.in_rows;
+        qp = p.q + (size_t)peer * p.in_peer + ((size_t)b * p.in_rows + sr) * rs + (size_t)h * D + 8 * g;
+      } else {
+        qp = p.q + ((size_t)b * p.Sq + qr) * rs + (size_t)h * D + 8 * g;
+      }
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const uint4 u = q_ok ? *reinterpret_cast<const uint4*>(qp + kk * 16) : make_uint4(0, 0, 0, 0);
@@ -257,20 +276,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
 
     auto issue = [&](int kb, char* kdst, char* vdst) __attribute__((always_inline)) {
       const int j0 = kb * kBN;
-      const uint16_t* kb_ptr = kbase + (size_t)j0 * rs;
-      const uint16_t* vb_ptr = vbase + (size_t)j0 * rs;
-      // bytes of this batch's keys from the block start, none for a block
-      // past kb1: loads beyond them are out of range, access no memory and
-      // fill their LDS bytes with zeros (finite; those scores are masked)
-      // (a scalar select, not a branch: the QK products and the weights stay
-      // in one scheduling region)
-      const uint32_t rows = kb < kb1 ? (uint32_t)max(skv - j0, 0) : 0u;
-      const int nrec = (int)min((uint64_t)rows * (uint64_t)(rs * 2), (uint64_t)0x7fffffff);
-      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb_ptr, (short)0, nrec, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb_ptr, (short)0, nrec, kBufferWord3);
+      size_t blk = (size_t)j0 * rs;  // element offset of the block's first row
+      uint32_t nrec;                 // bytes from the block start that may be read
+      uint32_t lim = kBN, jump = 0;  // kRecv: rows >= lim lie in the next peer's chunk
+      if constexpr (kRecv) {
+        // block rows before lim are rows s0.. of peer p0; the rest (in_rows
+        // >= kBN, so at most one boundary) continue at row 0 of peer p0 + 1,
+        // `jump` bytes further on; past the last peer's chunk nothing is read
+        const uint32_t p0 = fdiv((uint32_t)j0, p.in_div);
+        const uint32_t s0 = (uint32_t)j0 - p0 * (uint32_t)p.in_rows;
+        blk = (size_t)p0 * p.in_peer + (size_t)s0 * rs;
+        lim = (uint32_t)p.in_rows - s0;
+        jump = (uint32_t)((p.in_peer - (int64_t)p.in_rows * (int64_t)rs) * 2);
+        const uint32_t last = (uint32_t)min((uint64_t)lim * (uint64_t)(rs * 2), (uint64_t)0x7fffffff);
+        nrec = kb < kb1 ? ((int)p0 == p.in_last_peer ? last : 0x7fffffffu) : 0u;
+      } else {
+        // bytes of this batch's keys from the block start, none for a block
+        // past kb1: loads beyond them are out of range, access no memory and
+        // fill their LDS bytes with zeros (finite; those scores are masked)
+        // (a scalar select, not a branch: the QK products and the weights
+        // stay in one scheduling region)
+        const uint32_t rows = kb < kb1 ? (uint32_t)max(skv - j0, 0) : 0u;
+        nrec = (uint32_t)min((uint64_t)rows * (uint64_t)(rs * 2), (uint64_t)0x7fffffff);
+      }
+      const uint16_t* kb_ptr = kbase + blk;
+      const uint16_t* vb_ptr = vbase + blk;
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb_ptr, (short)0, (int)nrec, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb_ptr, (short)0, (int)nrec, kBufferWord3);
 #pragma unroll
       for (int u = 0; u < INSTR_W; ++u) {
-        const uint32_t off = ld_off[u];
+        uint32_t off = ld_off[u];
+        if constexpr (kRecv) off += (uint32_t)ld_row[u] >= lim ? jump : 0u;
         const int dst = (wave * INSTR_W + u) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + dst), 16, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + dst), 16, off, 0, 0, 0);
@@ -643,7 +679,7 @@ hipError_t occupancy_of(int dev, int* occ) {
   int n = cached[dev].load(std::memory_order_relaxed);
   if (n == 0) {
     const hipError_t e =
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<D, kOutF32, kMerge>, kThreads, 0);
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<D, kOutF32, kMerge, false>, kThreads, 0);
     if (e != hipSuccess) return e;
     if (n < 1) n = 1;
     cached[dev].store(n, std::memory_order_relaxed);
@@ -701,6 +737,10 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.send_rows = a.send_rows;
   p.send_batches = a.B;
   p.o_heads = a.send_rows > 0 ? a.o_heads : a.H;
+  p.in_rows = a.in_rows;
+  p.in_last_peer = a.in_peers - 1;
+  p.in_div = make_fastdiv(a.in_rows > 0 ? (uint32_t)a.in_rows : 1u);
+  p.in_peer = a.in_peer;
   if (pl.n_tiles == 0 || p.nblocks == 0) return hipSuccess;
   // without (enough) workspace every tile is taken whole
   const bool split = pl.split > 1 && a.workspace != nullptr && a.workspace_bytes >= pl.ws_bytes;
@@ -710,7 +750,14 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   p.cnt = split ? static_cast<int32_t*>(a.workspace) : nullptr;
   p.part = split ? reinterpret_cast<float*>(static_cast<char*>(a.workspace) + pl.cnt_bytes) : nullptr;
   const uint64_t grid = (uint64_t)p.n_whole + p.split_wgs;
-  attn_bf16_kernel<D, kOutF32, kMerge><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  if constexpr (!kOutF32 && !kMerge) {
+    if (a.in_rows > 0) {  // Q, K, V from the receive buffer (bf16 O only)
+      attn_bf16_kernel<D, false, false, true><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+      return hipGetLastError();
+    }
+  }
+  if (a.in_rows > 0) return hipErrorInvalidValue;
+  attn_bf16_kernel<D, kOutF32, kMerge, false><<<(unsigned)grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -716,7 +716,7 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
                        dit_dtype_t o_dtype, void* stream, bool merge, const int32_t* kv_len = nullptr,
                        bool has_kv_len = false, void* workspace = nullptr, int64_t workspace_bytes = 0,
                        bool static_scratch = false, const dit_a2a_layout* send = nullptr,
-                       int32_t send_rank = 0) {
+                       int32_t send_rank = 0, const dit_a2a_layout* recv = nullptr) {
   dit_status_t st = check_attn_shape(B, Sq, Skv, H, D, in_dtype, o_dtype);
   if (st != DIT_OK) return st;
   if (!(scale > 0.0f) || !isfinite(scale))
@@ -740,14 +740,17 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
     return fail(DIT_ERR_UNSUPPORTED, "q/k/v/o must be 16-byte aligned");
   if (lse != nullptr && !aligned(lse, 4)) return fail(DIT_ERR_UNSUPPORTED, "lse not 4-byte aligned");
   const int eb = dtype_bytes(in_dtype);
-  const size_t q_bytes = (size_t)B * Sq * H * D * eb;
-  const size_t kv_bytes = (size_t)B * Skv * H * D * eb;
+  // with a receive buffer, q is its start and the three planes lie inside it
+  const size_t q_bytes = recv != nullptr ? (size_t)recv->U * recv->elems_per_peer * eb : (size_t)B * Sq * H * D * eb;
+  const size_t kv_bytes = recv != nullptr ? 0 : (size_t)B * Skv * H * D * eb;
   // O is [B, Sq, H, D], or the whole send buffer [U, 1, B, S_loc, H, D]
   const size_t o_bytes = send != nullptr ? (size_t)send->U * send->elems_per_peer * 2
                                          : (size_t)B * Sq * H * D * dtype_bytes(o_dtype);
+  const size_t lse_bytes = (size_t)B * H * Sq * 4;
   if (overlap(o, o_bytes, q, q_bytes) || overlap(o, o_bytes, k, kv_bytes) ||
       overlap(o, o_bytes, v, kv_bytes) ||
-      (lse != nullptr && overlap(lse, (size_t)B * H * Sq * 4, o, o_bytes)))
+      (lse != nullptr && (overlap(lse, lse_bytes, o, o_bytes) || overlap(lse, lse_bytes, q, q_bytes) ||
+                          overlap(lse, lse_bytes, k, kv_bytes) || overlap(lse, lse_bytes, v, kv_bytes))))
     return fail(DIT_ERR_INVALID_ARGUMENT, "outputs overlap inputs");
   if (workspace != nullptr) {
     const size_t wb = (size_t)workspace_bytes;
@@ -775,6 +778,11 @@ dit_status_t attn_call(const void* q, const void* k, const void* v, void* o, flo
   if (send != nullptr) {
     a.send_rows = send->S_loc;
     a.o_heads = std::max(0, std::min(send->H_loc, send->H - send_rank * send->H_loc));
+  }
+  if (recv != nullptr) {
+    a.in_rows = recv->S_loc;
+    a.in_peers = recv->U;
+    a.in_peer = recv->elems_per_peer;
   }
   if (workspace != nullptr) {
     size_t need = 0;
@@ -853,6 +861,35 @@ dit_status_t dit_attn_fwd_send(const void* q, const void* k, const void* v, void
   return attn_call(q, k, v, send_buf, lse, layout->B, layout->S, Skv, layout->H_loc, layout->D, scale,
                    DIT_BF16, DIT_BF16, stream, false, nullptr, false, workspace, workspace_bytes, false,
                    layout, rank);
+}
+
+dit_status_t dit_attn_fwd_a2a(const void* recv_buf, void* send_buf, float* lse,
+                              const dit_a2a_layout* layout, int32_t rank, float scale, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+  dit_status_t st = check_permute(layout, DIT_SEQ_TO_HEAD, rank);
+  if (st != DIT_OK) return st;
+  if (layout->n_planes != 3)
+    return fail(DIT_ERR_INVALID_ARGUMENT, "the receive buffer holds three planes (Q, K, V); layout has n_planes = %d",
+                layout->n_planes);
+  if (layout->dtype != DIT_BF16)
+    return fail(DIT_ERR_UNSUPPORTED, "attention from the receive buffer is served for bf16 only");
+  if (layout->S_loc < 64)
+    return fail(DIT_ERR_UNSUPPORTED, "attention from the receive buffer needs S_loc >= 64 (S_loc = %d)",
+                layout->S_loc);
+  if ((int64_t)layout->B * layout->S * layout->H_loc == 0) {
+    clear_error();
+    return DIT_OK;
+  }
+  if (recv_buf == nullptr) return fail(DIT_ERR_INVALID_ARGUMENT, "recv_buf is NULL");
+  // O goes to the head-to-sequence send buffer: the same group with one plane
+  dit_a2a_layout out = *layout;
+  out.n_planes = 1;
+  out.elems_per_peer = layout->elems_per_peer / 3;
+  const int64_t plane = out.elems_per_peer;  // B * S_loc * H_loc * D
+  const uint16_t* q = static_cast<const uint16_t*>(recv_buf);
+  return attn_call(q, q + plane, q + 2 * plane, send_buf, lse, layout->B, layout->S, layout->S, layout->H_loc,
+                   layout->D, scale, DIT_BF16, DIT_BF16, stream, false, nullptr, false, workspace,
+                   workspace_bytes, false, &out, rank, layout);
 }
 
 dit_status_t dit_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,

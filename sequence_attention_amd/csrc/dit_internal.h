@@ -146,6 +146,13 @@ struct AttnArgs {
   // row t % send_rows), heads at or past o_heads as zeros.
   int32_t send_rows = 0;
   int32_t o_heads = 0;
+  // bf16 path, bf16 O only: in_rows > 0 reads Q, K and V from the
+  // sequence-to-head receive buffer [in_peers, 3, B, in_rows, H, D] (q, k,
+  // v at planes 0, 1, 2 of the first peer's chunk, in_peer elements between
+  // peers); in_rows >= 64.
+  int32_t in_rows = 0;
+  int32_t in_peers = 0;
+  int64_t in_peer = 0;
 };
 
 // Zero rows [t0, t1) (t1 <= U * S_loc) of every batch of a bf16 send buffer

@@ -307,6 +307,43 @@ def test_attn_fwd_send_rejects(lib):
     assert call(layout=ctypes.byref(empty), q_=NULL, send_=NULL) == 0
 
 
+def test_attn_fwd_a2a_rejects(lib):
+    # B=1, S=256, H=4, D=64 bf16, U=2: S_loc 128; recv [2,3,1,128,2,64] = 192 KiB, send 64 KiB
+    L = _layout(lib, 1, 256, 4, 64, 2, 1, 3, 0)
+    f = lib.dit_attn_fwd_a2a
+    recv, send, lse = P(A), P(A + 2**22), P(A + 2**23)
+
+    def call(layout=ctypes.byref(L), rank=0, scale=0.125, recv_=recv, send_=send, lse_=lse, ws=NULL, wsb=0):
+        return f(recv_, send_, ctypes.cast(lse_, ctypes.POINTER(ctypes.c_float)), layout, rank, scale,
+                 ws, wsb, NULL)
+
+    assert call(layout=None) == INV
+    assert call(rank=2) == INV
+    assert call(rank=-1) == INV
+    assert call(scale=0.0) == INV
+    assert call(scale=float("nan")) == INV
+    assert call(recv_=NULL) == INV
+    assert call(send_=NULL) == INV
+    assert call(send_=P(A + 3 * 2**16 - 1024)) == INV                     # send inside the recv buffer
+    assert call(lse_=P(A + 1024)) == INV                                  # lse inside the recv buffer
+    assert call(ws=P(A + 2**24 + 64), wsb=4096) == UNS                    # workspace alignment
+    assert call(ws=P(A + 256), wsb=4096) == INV                           # workspace inside recv
+    assert call(send_=P(A + 2**22 + 8)) == UNS                            # misaligned
+    L1 = _layout(lib, 1, 256, 4, 64, 2, 1, 1, 0)
+    assert call(layout=ctypes.byref(L1)) == INV                           # n_planes must be 3
+    Lh = _layout(lib, 1, 256, 4, 64, 2, 1, 3, 1)
+    assert call(layout=ctypes.byref(Lh)) == UNS                           # f16 buffer
+    Ls = _layout(lib, 1, 100, 4, 64, 2, 1, 3, 0)
+    assert call(layout=ctypes.byref(Ls)) == UNS                           # S_loc 50 < 64
+    Ld = _layout(lib, 1, 256, 4, 96, 2, 1, 3, 0)
+    assert call(layout=ctypes.byref(Ld)) == UNS                           # head dim
+    bad = _lib.DitA2ALayout.from_buffer_copy(L)
+    bad.elems_per_peer += 1
+    assert call(layout=ctypes.byref(bad)) == INV
+    empty = _layout(lib, 0, 256, 4, 64, 2, 1, 3, 0)
+    assert call(layout=ctypes.byref(empty), recv_=NULL, send_=NULL) == 0
+
+
 def _ws_size(lib, B=1, Sq=128, Skv=128, H=2, D=64, din=0, dout=0, merge=0, out=True):
     n = ctypes.c_int64(-5)
     st = lib.dit_attn_workspace_size(B, Sq, Skv, H, D, din, dout, merge, ctypes.byref(n) if out else None)
