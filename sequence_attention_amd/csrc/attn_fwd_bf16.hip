@@ -274,6 +274,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
       }
     }
 
+    // kRecv: peer, local row and element offset of the next block to issue
+    // (blocks are issued in increasing order, one at a time)
+    uint32_t nx_p = 0, nx_s = 0;
+    size_t nx_blk = 0;
+    if constexpr (kRecv) {
+      const uint32_t j = (uint32_t)kb0 * kBN;
+      nx_p = fdiv(j, p.in_div);
+      nx_s = j - nx_p * (uint32_t)p.in_rows;
+      nx_blk = (size_t)nx_p * p.in_peer + (size_t)nx_s * rs;
+    }
     auto issue = [&](int kb, char* kdst, char* vdst) __attribute__((always_inline)) {
       const int j0 = kb * kBN;
       size_t blk = (size_t)j0 * rs;  // element offset of the block's first row
@@ -283,10 +293,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
         // block rows before lim are rows s0.. of peer p0; the rest (in_rows
         // >= kBN, so at most one boundary) continue at row 0 of peer p0 + 1,
         // `jump` bytes further on; past the last peer's chunk nothing is read
-        const uint32_t p0 = fdiv((uint32_t)j0, p.in_div);
-        const uint32_t s0 = (uint32_t)j0 - p0 * (uint32_t)p.in_rows;
-        blk = (size_t)p0 * p.in_peer + (size_t)s0 * rs;
+        const uint32_t p0 = nx_p, s0 = nx_s;
+        blk = nx_blk;
         lim = (uint32_t)p.in_rows - s0;
+        nx_s = s0 + kBN;
+        nx_blk += (size_t)kBN * rs;
+        if (nx_s >= (uint32_t)p.in_rows) {
+          nx_s -= (uint32_t)p.in_rows;
+          nx_p += 1;
+          nx_blk += (size_t)p.in_peer - (size_t)p.in_rows * rs;
+        }
         jump = (uint32_t)((p.in_peer - (int64_t)p.in_rows * (int64_t)rs) * 2);
         const uint32_t last = (uint32_t)min((uint64_t)lim * (uint64_t)(rs * 2), (uint64_t)0x7fffffff);
         nrec = kb < kb1 ? ((int)p0 == p.in_last_peer ? last : 0x7fffffffu) : 0u;
