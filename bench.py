@@ -68,12 +68,14 @@ CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches 
 # that file reports traffic as null until the counters are taken again.
 ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
 ATTN_TRAFFIC = {
-    "src_sha256": "b3ef17fdc33795ee17b99ce306f1290393798028424dd4f490b320988c10857f",
-    # shape: (read bytes, write bytes) per launch
-    "per_shape": {"flux": (52_184_064, 14_378_496), "qwen_u4": (151_094_682, 55_741_235),
-                  "qwen_u5": (133_024_154, 45_326_131), "wan": (2_110_191_002, 98_287_206),
-                  "ring_chunk": (111_767_757, 61_251_584), "ring_unchunked": (262_763_315, 61_268_685),
-                  "ring_fused_hop": (137_265_152, 65_973_146)},
+    "src_sha256": "2df5e0ee3d69d5c401dfbb997dda4a0620943bf6d45744b0872125391986d844",
+    # shape: (read bytes, write bytes) per launch; flux_a2a is the step's
+    # attention from the receive buffer (dit_attn_fwd_a2a)
+    "per_shape": {"flux": (52_179_968, 14_377_062), "flux_a2a": (52_186_112, 14_377_472),
+                  "qwen_u4": (151_063_757, 55_742_874),
+                  "qwen_u5": (133_001_216, 45_325_926), "wan": (2_109_922_509, 98_289_050),
+                  "ring_chunk": (111_763_456, 61_231_002), "ring_unchunked": (262_688_358, 61_248_410),
+                  "ring_fused_hop": (137_263_104, 65_632_461)},
 }
 
 
