@@ -64,11 +64,12 @@ CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches 
 # HBM bytes per launch of the attention kernel, from two rocprofv3 --pmc
 # passes (FETCH_SIZE, WRITE_SIZE), each scaled by what the counter reads for
 # a device copy of known size (the factors are in the profile).  Valid only
-# for the kernel source they were taken on (SHA-256 below): any change to
-# that file reports traffic as null until the counters are taken again.
+# for the kernel code they were taken on (SHA-256 below, of the source with
+# its // comments and blank lines removed): any change to that code reports
+# traffic as null until the counters are taken again.
 ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
 ATTN_TRAFFIC = {
-    "src_sha256": "2df5e0ee3d69d5c401dfbb997dda4a0620943bf6d45744b0872125391986d844",
+    "src_sha256": "83f067632f2c302ace0763650b51cbf4532fe1c19e95c501f44a862866c52bd2",
     # shape: (read bytes, write bytes) per launch; flux_a2a is the step's
     # attention from the receive buffer (dit_attn_fwd_a2a)
     "per_shape": {"flux": (52_179_968, 14_377_062), "flux_a2a": (52_186_112, 14_377_472),
@@ -177,16 +178,24 @@ def hbm_entry(nbytes, us, **extra):
     return d
 
 
+def attn_code_sha256(path=None):
+    """SHA-256 of the attention kernel source without // comments, trailing
+    blanks and empty lines: a comment edit keeps the counters valid, any
+    change to the code does not."""
+    import hashlib
+    with open(path or ATTN_SRC, encoding="utf-8") as f:
+        lines = [ln.split("//", 1)[0].rstrip() for ln in f.read().splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
+
+
 def attn_traffic(shape_name):
     """Counter-measured HBM bytes per attention launch at this shape, or
     None when the kernel source changed since the counters were taken."""
-    import hashlib
     per = ATTN_TRAFFIC["per_shape"].get(shape_name)
     if per is None or ATTN_TRAFFIC["src_sha256"] is None:
         return None
-    with open(ATTN_SRC, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != ATTN_TRAFFIC["src_sha256"]:
-            return None
+    if attn_code_sha256() != ATTN_TRAFFIC["src_sha256"]:
+        return None
     return per[0] + per[1]
 
 

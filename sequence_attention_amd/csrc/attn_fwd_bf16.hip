@@ -47,8 +47,16 @@
 //    rescale the dominant weight of a near one-hot row is not exactly 1, and
 //    normalising by the unrounded sum would leave its rounding error
 //    (2^-9 |v|) in O.  LSE takes the sum of the unrounded weights.  Tail
-//    keys past Skv are clamped on load and masked to -inf; tail query rows
-//    are never stored.
+//    keys past Skv read as zeros (out of the descriptor range) and are
+//    masked to -inf; tail query rows are never stored.
+//  * Inside a block the operand reads are pinned against the MFMAs with
+//    scheduling-group barriers: four K reads in flight, then one per QK
+//    MFMA; eight V reads in flight, then two per PV MFMA.
+//  * Layouts: Q, K, V as [B, S, H, D] tensors, or (kRecv) as the three
+//    planes of the Ulysses sequence-to-head receive buffer (edge-dit.cpp
+//    "Parallel execution": the received, peer-major buffer is decoded by
+//    the attention's own addressing instead of an unpack pass); O to
+//    [B, Sq, H, D] or straight into the head-to-sequence send buffer.
 //  * Work tiles are renumbered so that consecutive query tiles of one head
 //    land on the same XCD (workgroups are dealt round-robin over the 8
 //    XCDs): the head's K/V stream is then served from that XCD's L2.
