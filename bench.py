@@ -957,7 +957,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
-    clock = {"fma": sa.dit_clock_probe(), "mfma": sa.dit_clock_probe(mfma=True, spin=5000)}
+    clock = {"fma": sa.dit_clock_probe(), "mfma": sa.dit_clock_probe(mfma=True, spin=5000),
+             "mfma_sustained": sa.dit_clock_probe(mfma=True, spin=80000)}
     progress(f"timed steps done: {ms_per_step:.4f} ms/step")
 
     # the same K steps replayed from one captured graph
@@ -989,7 +990,9 @@ def main():
                                                 for m, c in clock.items()},
                           "method": "dit_clock_probe right after the region: s_memtime cycles / "
                                     "s_memrealtime (100 MHz) ticks per workgroup, 256 workgroups, "
-                                    "median / min / max; fma = light load, mfma = bf16 MFMA load"},
+                                    "median / min / max; fma = light load, mfma = bf16 MFMA load "
+                                    "(~0.3 ms), mfma_sustained = the same MFMA load for ~5 ms, "
+                                    "long enough for the power limit to set the clock"},
         "ms_per_step_graph": round(steps_graph_us / 1e3, 4),
         "roofline": attn_roofline(w.name + "_a2a", attn_flop, attn_us,
                                   kernel="attn_bf16_kernel<128, false, false, true> (dit_attn_fwd_a2a)"),
