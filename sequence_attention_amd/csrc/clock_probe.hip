@@ -20,11 +20,19 @@ __global__ __launch_bounds__(256) void clock_probe_kernel(int64_t* out, int32_t 
   const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
   float live;
   if constexpr (kMfma) {
-    // four independent accumulators keep the matrix pipe of each SIMD full
+    // four independent accumulators keep the matrix pipe of each SIMD full;
+    // the operands are pseudo-random bf16 values of either sign in [1, 2)
+    // with all mantissa bits in play (operands with empty mantissas, such as
+    // small multiples of 1/8, draw visibly less power and let the clock
+    // stay higher than attention's score and value data do)
     bf16x8 a, b;
+    uint32_t h = threadIdx.x * 0x9E3779B9u + blockIdx.x * 0x85EBCA6Bu + 1u;
     for (int e = 0; e < 8; ++e) {
-      a[e] = (__bf16)((float)(threadIdx.x & 7) * 0.125f);
-      b[e] = (__bf16)((float)(e + 1) * 0.0625f);
+      h ^= h << 13;
+      h ^= h >> 17;
+      h ^= h << 5;
+      a[e] = __builtin_bit_cast(__bf16, (uint16_t)((h & 0x807Fu) | 0x3F80u));
+      b[e] = __builtin_bit_cast(__bf16, (uint16_t)(((h >> 16) & 0x807Fu) | 0x3F80u));
     }
     f32x16 acc[4];
     for (int j = 0; j < 4; ++j)
