@@ -995,7 +995,7 @@ def main():
                                     "long enough for the power limit to set the clock"},
         "ms_per_step_graph": round(steps_graph_us / 1e3, 4),
         "roofline": attn_roofline(w.name + "_a2a", attn_flop, attn_us,
-                                  kernel="attn_bf16_kernel<128, false, false, true> (dit_attn_fwd_a2a)"),
+                                  kernel="attn_bf16_kernel<128, false, false, 2> (dit_attn_fwd_a2a, chunk of whole key blocks)"),
         "kernels": kernels,
     }
     result["roofline"].pop("flop", None)

@@ -52,11 +52,13 @@
 //  * Inside a block the operand reads are pinned against the MFMAs with
 //    scheduling-group barriers: four K reads in flight, then one per QK
 //    MFMA; eight V reads in flight, then two per PV MFMA.
-//  * Layouts: Q, K, V as [B, S, H, D] tensors, or (kRecv) as the three
+//  * Layouts: Q, K, V as [B, S, H, D] tensors, or (kIn 1, 2) as the three
 //    planes of the Ulysses sequence-to-head receive buffer (edge-dit.cpp
 //    "Parallel execution": the received, peer-major buffer is decoded by
-//    the attention's own addressing instead of an unpack pass); O to
-//    [B, Sq, H, D] or straight into the head-to-sequence send buffer.
+//    the attention's own addressing instead of an unpack pass; with a chunk
+//    length that is a multiple of 64 no key block straddles two peers and
+//    the per-lane peer select is compiled out); O to [B, Sq, H, D] or
+//    straight into the head-to-sequence send buffer.
 //  * Work tiles are renumbered so that consecutive query tiles of one head
 //    land on the same XCD (workgroups are dealt round-robin over the 8
 //    XCDs): the head's K/V stream is then served from that XCD's L2.
@@ -171,8 +173,12 @@ constexpr size_t slot_floats() {
   return (size_t)kWaves * 64 * (D / 2 + 4);
 }
 
-template <int D, bool kOutF32, bool kMerge, bool kRecv>
+// kIn: 0 Q, K, V as [B, S, H, D] tensors; 1 planes of the receive buffer;
+// 2 the same when the chunk length is a multiple of the key block (no
+// block then straddles two peers, and the per-lane peer select is dropped).
+template <int D, bool kOutF32, bool kMerge, int kIn>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
+  constexpr bool kRecv = kIn != 0;
   constexpr int ROWB = D * 2;                 // bytes of one K/V row
   constexpr int BLKB = kBN * ROWB;            // bytes of one K or V block
   constexpr int NINSTR = BLKB / 1024;         // 1 KB direct loads per tensor per block
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(Params p) {
 #pragma unroll
       for (int u = 0; u < INSTR_W; ++u) {
         uint32_t off = ld_off[u];
-        if constexpr (kRecv) off += (uint32_t)ld_row[u] >= lim ? jump : 0u;
+        if constexpr (kIn == 1) off += (uint32_t)ld_row[u] >= lim ? jump : 0u;
         const int dst = (wave * INSTR_W + u) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + dst), 16, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + dst), 16, off, 0, 0, 0);
@@ -703,7 +709,7 @@ hipError_t occupancy_of(int dev, int* occ) {
   int n = cached[dev].load(std::memory_order_relaxed);
   if (n == 0) {
     const hipError_t e =
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<D, kOutF32, kMerge, false>, kThreads, 0);
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<D, kOutF32, kMerge, 0>, kThreads, 0);
     if (e != hipSuccess) return e;
     if (n < 1) n = 1;
     cached[dev].store(n, std::memory_order_relaxed);
@@ -776,12 +782,15 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
   const uint64_t grid = (uint64_t)p.n_whole + p.split_wgs;
   if constexpr (!kOutF32 && !kMerge) {
     if (a.in_rows > 0) {  // Q, K, V from the receive buffer (bf16 O only)
-      attn_bf16_kernel<D, false, false, true><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+      if (a.in_rows % kBN == 0)
+        attn_bf16_kernel<D, false, false, 2><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+      else
+        attn_bf16_kernel<D, false, false, 1><<<(unsigned)grid, kThreads, 0, stream>>>(p);
       return hipGetLastError();
     }
   }
   if (a.in_rows > 0) return hipErrorInvalidValue;
-  attn_bf16_kernel<D, kOutF32, kMerge, false><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  attn_bf16_kernel<D, kOutF32, kMerge, 0><<<(unsigned)grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@ head-to-sequence send buffer.
 Bit-exact against the unfused chain it replaces (dit_ulysses_unpack of the
 receive buffer, then dit_attn_fwd_send with the same workspace setting), on
 every rank of ragged layouts: S_loc not a multiple of the 64-key block (key
-blocks that straddle two source peers), pad rows on the last peers, pad
+blocks that straddle two source peers) and S_loc a multiple of it (the
+kernel form without the peer select), pad rows on the last peers, pad
 heads, U = 1, seq_align 64; with and without the workspace that splits the
 last round.  The receive buffers are random everywhere, pad rows and pad
 heads included, so nothing of the pads may leak into O or LSE.  Against the
@@ -65,6 +66,9 @@ CASES = [
     (1, 333, 4, 128, 4, 64),    # seq_align 64: S_loc 96, pad rows over two peers
     (2, 257, 4, 64, 1, 1),      # U = 1
     (1, 1000, 4, 64, 3, 1),     # three peers, S_loc 334
+    (1, 256, 4, 128, 2, 1),     # S_loc 128: chunks of whole key blocks (no peer select)
+    (2, 384, 3, 64, 3, 1),      # S_loc 128, three peers, D = 64
+    (1, 500, 5, 128, 4, 64),    # seq_align 64: S_loc 128, pad rows on the last peer
 ]
 
 
