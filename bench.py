@@ -69,14 +69,14 @@ CFG_SHAPE = (2, 4096, 64)     # FLUX 1024x1024 latent prediction: 64x64 patches 
 # traffic as null until the counters are taken again.
 ATTN_SRC = os.path.join(ROOT, "sequence_attention_amd", "csrc", "attn_fwd_bf16.hip")
 ATTN_TRAFFIC = {
-    "src_sha256": "83f067632f2c302ace0763650b51cbf4532fe1c19e95c501f44a862866c52bd2",
+    "src_sha256": "66985ac27e3210730afbaec9b7c0c346b43b9c08830a50f1822cef183f8b33d5",
     # shape: (read bytes, write bytes) per launch; flux_a2a is the step's
     # attention from the receive buffer (dit_attn_fwd_a2a)
-    "per_shape": {"flux": (52_179_968, 14_377_062), "flux_a2a": (52_186_112, 14_377_472),
-                  "qwen_u4": (151_063_757, 55_742_874),
-                  "qwen_u5": (133_001_216, 45_325_926), "wan": (2_109_922_509, 98_289_050),
-                  "ring_chunk": (111_763_456, 61_231_002), "ring_unchunked": (262_688_358, 61_248_410),
-                  "ring_fused_hop": (137_263_104, 65_632_461)},
+    "per_shape": {"flux": (52_175_872, 14_377_165), "flux_a2a": (52_184_064, 14_377_677),
+                  "qwen_u4": (151_069_082, 55_749_222),
+                  "qwen_u5": (133_027_021, 45_325_619), "wan": (2_109_947_699, 98_289_254),
+                  "ring_chunk": (111_770_214, 61_230_694), "ring_unchunked": (262_763_315, 61_251_686),
+                  "ring_fused_hop": (137_255_117, 65_658_163)},
 }
 
 
