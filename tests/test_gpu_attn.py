@@ -257,6 +257,25 @@ def test_split_tiles_and_workspace_reuse():
     assert torch.count_nonzero(ws[:65536]).item() == 0   # counters left zero
 
 
+def test_split_merge_does_not_depend_on_arrival_order():
+    # the ring chunk's last 128 tiles are cut in two equal halves that reach
+    # the merge in either order; the last to arrive merges both slots in key
+    # order, so repeated calls agree exactly
+    B, Sq, Skv, H, D = 1, 4096, 4096, 24, 128
+    log(f"attn bf16 split merge, repeated {(B, Sq, Skv, H, D)}")
+    w = workloads.Workload("two", B=B, Sq=Sq, Skv=Skv, H=H, D=D, R=1, S=Skv, H_total=H, U=1)
+    q, k, v = (t.to(DEV) for t in workloads.attention_inputs(w, seed=7))
+    need = sa.dit_attn_workspace_size(B, Sq, Skv, H, D)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    runs = [sa.dit_attn_fwd_ws(q, k, v, ws, scale=w.scale) for _ in range(4)]
+    torch.cuda.synchronize()
+    for o, lse in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), runs[0][1].view(torch.int32))
+    assert torch.count_nonzero(ws[:65536]).item() == 0
+
+
 def test_workspace_smaller_than_needed_is_rejected():
     B, Sq, Skv, H, D = SPLIT_SEQUENCE[0]
     need = sa.dit_attn_workspace_size(B, Sq, Skv, H, D)
