@@ -65,3 +65,10 @@ def max_abs(a: np.ndarray, b: np.ndarray) -> float:
     if a.size == 0:
         return 0.0
     return float(np.max(np.abs(a - b)))
+
+
+def bf16_half_spacing(x: np.ndarray) -> np.ndarray:
+    """Half the distance between adjacent bf16 values around |x| (8
+    significand bits): for |x| in [2^(E-1), 2^E) the spacing is 2^(E-8)."""
+    _, e = np.frexp(np.abs(x))
+    return np.where(x == 0, 0.0, np.ldexp(1.0, e - 9))

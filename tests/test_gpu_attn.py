@@ -26,7 +26,7 @@ import torch
 import oracle
 import sequence_attention_amd as sa
 from sequence_attention_amd import workloads
-from tests.gpu_util import DEV, Guarded, log, max_abs
+from tests.gpu_util import bf16_half_spacing, DEV, Guarded, log, max_abs
 
 pytestmark = pytest.mark.gpu
 
@@ -45,13 +45,6 @@ def run_attn(q, k, v, scale=None, o_dtype=None, lse=True):
     if lse:
         assert l.canary_ok(), "write past the end of LSE"
     return o.t, (l.t if lse else None)
-
-
-def bf16_half_spacing(x: np.ndarray) -> np.ndarray:
-    """Half the distance between adjacent bf16 values around |x| (8
-    significand bits): for |x| in [2^(E-1), 2^E) the spacing is 2^(E-8)."""
-    _, e = np.frexp(np.abs(x))
-    return np.where(x == 0, 0.0, np.ldexp(1.0, e - 9))
 
 
 def check(o, lse, q, k, v, scale, rows=None, dtype=torch.bfloat16, what="", out_rounding=False):
