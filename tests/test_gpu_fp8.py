@@ -48,7 +48,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES)
+def _random_cases(n_cases, seed=53):
+    # seeded sweep: heads of 1 to 4 scale blocks, ragged S and H, U above
+    # and below H, every alignment
+    r = np.random.default_rng(seed)
+    return [(int(r.integers(1, 3)), int(r.integers(1, 300)), int(r.integers(1, 9)), int(r.choice([32, 64, 96, 128])),
+             int(r.integers(1, 6)), int(r.choice([1, 4, 64]))) for _ in range(n_cases)]
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(10))
 def test_all_ranks_fp8_exchange_matches_oracle(case):
     B, S, H, D, U, al = case
     log(f"fp8 exchange {case}")

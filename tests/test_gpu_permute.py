@@ -49,7 +49,23 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("case", SMALL)
+def _random_cases(n_cases, seed=77):
+    # a seeded sweep over the same parameters: any head size (2-byte to
+    # 16-byte vectors), U above and below H, every alignment, both dtypes
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_cases):
+        out.append((int(r.integers(1, 4)), int(r.integers(1, 300)), int(r.integers(1, 10)),
+                    int(r.choice([1, 2, 3, 6, 8, 16, 24, 40, 64, 128])), int(r.integers(1, 7)),
+                    int(r.choice([1, 4, 64])), int(r.choice([1, 3])),
+                    torch.float32 if r.random() < 0.3 else torch.bfloat16))
+    return out
+
+
+RANDOM = _random_cases(16)
+
+
+@pytest.mark.parametrize("case", SMALL + RANDOM)
 def test_all_ranks_round_trip_matches_oracle(case):
     B, S, H, D, U, al, n, dt = case
     log(f"permute all-ranks {case}")

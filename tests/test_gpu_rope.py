@@ -72,7 +72,19 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES)
+def _random_cases(n_cases, seed=29):
+    # seeded sweep: ragged S and H, U above and below H, head sizes of one
+    # to eight 16-byte vectors, the three dtypes
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_cases):
+        dt = [torch.bfloat16, torch.float16, torch.float32][int(r.integers(0, 3))]
+        D = int(r.choice([8, 16, 24, 64, 128] if dt != torch.float32 else [4, 8, 12, 64]))
+        out.append((int(r.integers(1, 3)), int(r.integers(1, 300)), int(r.integers(1, 9)), D, int(r.integers(1, 6)), dt))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(10))
 def test_all_ranks_match_oracle(case):
     B, S, H, D, U, dt = case
     log(f"rope unpack {case}")

@@ -57,7 +57,24 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES)
+def _random_cases(n_cases, seed=91):
+    # seeded sweep: random per-rank sequence and head counts (ranks with no
+    # rows or no heads included) or the default split, any head size, the
+    # three dtypes
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_cases):
+        B, S, H, U = int(r.integers(1, 3)), int(r.integers(1, 200)), int(r.integers(1, 9)), int(r.integers(1, 6))
+        D = int(r.choice([1, 2, 3, 4, 8, 16, 24, 64]))
+        n = int(r.choice([1, 3]))
+        dt = [torch.bfloat16, torch.float16, torch.float32][int(r.integers(0, 3))]
+        seq = [int(x) for x in r.multinomial(S, r.dirichlet(np.ones(U)))] if r.random() < 0.6 else None
+        heads = [int(x) for x in r.multinomial(H, r.dirichlet(np.ones(U)))] if r.random() < 0.6 else None
+        out.append((B, S, H, D, U, n, dt, seq, heads))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(12))
 def test_all_ranks_round_trip_matches_oracle(case):
     B, S, H, D, U, n, dt, sc, hc = case
     log(f"uneven all-ranks {case}")
