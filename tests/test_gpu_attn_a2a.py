@@ -72,7 +72,20 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES)
+def _random_cases(n_cases, seed=61):
+    # seeded sweep: chunks of 64 to ~200 rows (whole key blocks or not),
+    # pad rows and pad heads, both head sizes, U = 1..4
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_cases):
+        U = int(r.integers(1, 5))
+        S = int(r.integers(64 * U, 64 * U + 500))
+        out.append((int(r.integers(1, 3)), S, int(r.integers(1, 8)), int(r.choice([64, 128])), U,
+                    int(r.choice([1, 64]))))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(8))
 @pytest.mark.parametrize("ws", [True, False], ids=["split", "whole"])
 def test_all_ranks_bitwise_and_oracle(case, ws):
     B, S, H, D, U, al = case

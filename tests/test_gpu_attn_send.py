@@ -63,7 +63,20 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES)
+def _random_cases(n_cases, seed=67):
+    # seeded sweep: ragged S and H, U above and below H, both head sizes,
+    # both alignments, key counts other than S
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_cases):
+        S = int(r.integers(1, 700))
+        skv = None if r.random() < 0.5 else int(r.integers(1, 900))
+        out.append((int(r.integers(1, 3)), S, int(r.integers(1, 9)), int(r.choice([64, 128])), int(r.integers(1, 6)),
+                    int(r.choice([1, 64])), skv))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(8))
 def test_all_ranks_bitwise_and_oracle(case):
     B, S, H, D, U, al, Skv = case
     Skv = S if Skv is None else Skv
