@@ -1,8 +1,9 @@
 """fp64 CPU oracle for the sequence-parallel DiT attention hot path.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product package imports, links or
-calls this package; only the test suite, the graft smoke check and the
-``cpu_baseline`` leg of ``bench.py`` may use it.  It shares no code, header,
+calls this package; only the test suite, ``smoke()`` in
+``__graft_entry__.py`` and the ``cpu_baseline`` leg of ``bench.py`` may use
+it.  It shares no code, header,
 table or helper with the HIP library: it is written from the source pages'
 definitions, in float64, with numpy as the only numerical library.
 
