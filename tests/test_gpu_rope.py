@@ -25,6 +25,10 @@ from tests.gpu_util import DEV, bits, log, simulate_all_to_all
 pytestmark = pytest.mark.gpu
 
 HALF_ULP = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11, torch.float32: 2.0 ** -23}
+# half the spacing of the subnormals: below the smallest normal the rounding
+# error of a correctly rounded result is bounded in absolute terms, not by
+# HALF_ULP * |x| (float16 subnormals are 2^-24 apart, below 2^-14)
+HALF_SUB = {torch.bfloat16: 2.0 ** -134, torch.float16: 2.0 ** -25, torch.float32: 2.0 ** -150}
 
 
 def _exchange(B, S, H, D, U, dtype, seed):
@@ -46,7 +50,7 @@ def _exchange(B, S, H, D, U, dtype, seed):
 
 
 def _check_rotated(got, ref, x_pairs_abs, dtype, what):
-    bound = HALF_ULP[dtype] * np.abs(ref) + 2.0 ** -22 * x_pairs_abs
+    bound = HALF_ULP[dtype] * np.abs(ref) + HALF_SUB[dtype] + 2.0 ** -22 * x_pairs_abs
     excess = np.max(np.abs(got - ref) - bound) if got.size else -1.0
     assert excess <= 0, f"{what}: rotated values off by {excess:.3e} beyond the bound"
 
@@ -103,6 +107,28 @@ def test_all_ranks_match_oracle(case):
             x = plain[pl].float().cpu().numpy().astype(np.float64)
             _check_rotated(got[pl].float().cpu().numpy().astype(np.float64), ref[pl], _pair_abs(x), dt,
                            f"rank {r} plane {pl}")
+
+
+def test_float16_results_in_the_subnormal_range():
+    # inputs of about 1e-5 rotate to float16 results below 2^-14, where one
+    # final rounding is bounded by half the subnormal spacing (2^-25)
+    B, S, H, D, U = 1, 64, 4, 64, 2
+    log("rope unpack float16 subnormal results")
+    L = sa.dit_a2a_layout_init(B, S, H, D, U, 1, 3, torch.float16)
+    Lo = oracle.a2a_layout(B, S, H, D, U, 1, 3)
+    g = torch.Generator().manual_seed(5)
+    recv = (torch.randn(U * L.elems_per_peer, generator=g) * 1e-5).to(torch.float16)
+    assert (recv.abs() < 2.0 ** -14).float().mean() > 0.9        # mostly subnormal inputs
+    cos, sin = workloads.rope_tables(S, D)
+    for r in range(U):
+        got = sa.dit_ulysses_unpack_rope(L, r, recv.to(DEV), cos.to(DEV), sin.to(DEV))
+        torch.cuda.synchronize()
+        rv = recv.float().numpy()
+        ref = oracle.unpack_seq_to_head_rope(rv, Lo, r, cos.numpy(), sin.numpy())
+        x = oracle.unpack_seq_to_head(rv, Lo, r)
+        for pl in range(3):
+            _check_rotated(got[pl].float().cpu().numpy().astype(np.float64), ref[pl], _pair_abs(x[pl]),
+                           torch.float16, f"subnormal rank {r} plane {pl}")
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16, torch.float32])
