@@ -63,6 +63,23 @@ def test_bf16_rounds_the_fp32_result(n):
     np.testing.assert_array_equal(bits(out.t), bits(want))
 
 
+def test_random_guidance_scales_and_magnitudes_bit_exact():
+    # 60 seeded calls: guidance scales from tiny to hundreds (and 0, +-1),
+    # inputs from 1e-30 to 1e30, ragged lengths; every fp32 result equals the
+    # oracle's correctly rounded fmaf(g, c - u, u)
+    r = np.random.default_rng(777)
+    for i in range(60):
+        n = int(r.integers(1, 5000))
+        g = float(np.float32(r.choice([r.normal() * 5, r.normal() * 100, r.uniform(-1e-3, 1e-3), 0.0, 1.0, -1.0])))
+        sc = float(r.choice([1e-30, 1e-3, 1.0, 1e3, 1e30]))
+        u = torch.from_numpy(r.standard_normal(n).astype(np.float32)) * sc
+        c = torch.from_numpy(r.standard_normal(n).astype(np.float32)) * sc
+        out = _run(u.to(DEV), c.to(DEV), g)
+        want = oracle.cfg_combine_f32(u.numpy(), c.numpy(), g)
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.int32), want.view(np.int32),
+                                      err_msg=f"case {i}: n={n} g={g} scale={sc}")
+
+
 def test_empty_is_a_no_op():
     u = torch.zeros(0, device=DEV)
     out = _run(u, u, 4.0)

@@ -79,8 +79,21 @@ SMALL = [
 ]
 
 
+def _random_cases(n_cases, seed=4242):
+    # seeded sweep: any head size (1 to 8 floats per thread), ragged S and H,
+    # U above and below H, every alignment, planes at 0, 4 and 8 bytes past
+    # a 16-byte boundary
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_cases):
+        D = int(r.choice([1, 2, 3, 4, 6, 8, 12, 16, 24, 64, 128]))
+        out.append((int(r.integers(1, 3)), int(r.integers(1, 200)), int(r.integers(1, 9)), D, int(r.integers(1, 6)),
+                    int(r.choice([1, 4, 64])), int(r.choice([1, 3])), int(r.choice([0, 1, 2]))))
+    return out
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "f16"])
-@pytest.mark.parametrize("case", SMALL)
+@pytest.mark.parametrize("case", SMALL + _random_cases(8))
 def test_all_ranks_match_oracle(case, fmt):
     B, S, H, D, U, al, n, off = case
     tdt, code = FMT[fmt]
