@@ -1,6 +1,8 @@
-"""Host logic of bench.py that needs no GPU: the refusal of more than one GPU
-and the keying of the counter-measured attention traffic to the kernel code
-(a comment edit keeps it, a code edit drops it to null)."""
+"""Host logic of bench.py that needs no GPU: the refusal of more than one GPU,
+the keying of the counter-measured attention traffic to the kernel code (a
+comment edit keeps it, a code edit drops it to null), and the summaries the
+profile tables are made from (kernel names shortened, medians of rocprofv3
+counter rows per kernel and grid)."""
 
 import os
 import subprocess
@@ -40,3 +42,28 @@ def test_traffic_reported_only_for_known_shapes():
     else:
         assert t is None
     assert bench.attn_traffic("no_such_shape") is None
+
+
+def test_kernel_short_name_cuts_the_parameter_list_outside_templates():
+    full = ("void dit::(anonymous namespace)::attn_bf16_kernel<128, false, false, 2>"
+            "(dit::(anonymous namespace)::Params)")
+    assert bench.kernel_short_name(full) == "attn_bf16_kernel<128, false, false, 2>"
+    vec = "void dit::(anonymous namespace)::permute_kernel<0, unsigned int __vector(4)>(dit::PermuteGeom)"
+    assert bench.kernel_short_name(vec) == "permute_kernel<0, u32x4>"
+    assert bench.kernel_short_name("plain") == "plain"
+
+
+def test_pmc_summary_takes_the_median_per_kernel_grid_and_counter(tmp_path, capsys):
+    k = "void dit::(anonymous namespace)::merge_kernel<false, 128>(void*, float*, void const*, float const*, int, int, int)"
+    rows = [("Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value")]
+    rows += [(k, "786432", "FETCH_SIZE", v) for v in ("10", "30", "20")]
+    rows += [(k, "786432", "WRITE_SIZE", "5")]
+    rows += [("void at::native::some_torch_kernel(int)", "64", "FETCH_SIZE", "999")]     # torch's: dropped
+    rows += [("__amd_rocclr_copyBuffer", "131072", "FETCH_SIZE", "7")]                    # the device copy: kept
+    csv_path = tmp_path / "c.csv"
+    csv_path.write_text("\n".join(",".join(f'"{x}"' for x in r) for r in rows) + "\n")
+    bench.pmc_summary(str(csv_path))
+    out = capsys.readouterr().out
+    assert "| merge_kernel<false, 128> | 786432 | FETCH_SIZE | 3 | 20.0 |" in out
+    assert "| merge_kernel<false, 128> | 786432 | WRITE_SIZE | 1 | 5.0 |" in out
+    assert "__amd_rocclr_copyBuffer" in out and "some_torch_kernel" not in out
