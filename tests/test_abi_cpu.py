@@ -208,6 +208,11 @@ def _attn(lib, q=A, k=A + 2**24, v=A + 2**25, o=A + 2**26, lse=A + 2**27, B=1, S
     (dict(lse=A + 2**27 + 2), UNS),
     (dict(o=A + 1024), INV),                        # o overlaps q
     (dict(lse=A + 2**26 + 64), INV),                # lse overlaps o
+    # size limits, checked before any pointer
+    (dict(B=65536, H=32768), UNS),                  # 2^31 query tiles of 128 rows
+    (dict(H=131072), UNS),                          # 64-row K/V block of 2^30 bytes
+    (dict(din=2, dout=2, H=65536), UNS),            # fp32 path: H on a grid axis of 65535
+    (dict(din=2, dout=2, B=65536), UNS),            # ... and B
 ])
 def test_attn_rejects(lib, kw, code):
     assert _attn(lib, **kw) == code, lib.dit_last_error()
